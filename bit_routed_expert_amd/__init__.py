@@ -1,0 +1,166 @@
+"""Python binding of the MI355X sparse MoE layer library (libstrata_moe.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  There is
+no fallback: if the shared library is missing or a call fails, an error is
+raised.
+
+The C ABI is declared in include/strata_moe.h; the names here mirror it:
+``workspace_bytes``, ``route``, ``forward``, ``kernel_names``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstrata_moe.so")
+
+STRATA_OK, STRATA_EINVAL, STRATA_EUNSUPPORTED, STRATA_EWORKSPACE, STRATA_EHIP = range(5)
+X_BF16, X_F32 = 0, 1
+NORM_FIRST = 1
+
+
+class StrataError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"strata_moe status {status}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("resident_mask", ctypes.c_void_p)]
+
+
+class RouteOut(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libstrata_moe.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_routed_expert_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.strata_moe_workspace_bytes.restype = sz
+    lib.strata_moe_workspace_bytes.argtypes = [ctypes.POINTER(Shape), i32, i32]
+    lib.strata_moe_route.restype = ctypes.c_int
+    lib.strata_moe_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), vp, ctypes.c_int, i32,
+                                     ctypes.POINTER(RouteOut), vp, sz, vp]
+    lib.strata_moe_forward.restype = ctypes.c_int
+    lib.strata_moe_forward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), i32, vp, ctypes.c_int, i32,
+                                       ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32, vp, vp, sz,
+                                       ctypes.POINTER(ctypes.c_void_p), i32, vp]
+    lib.strata_moe_kernel_names.restype = i32
+    lib.strata_moe_kernel_names.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(ctypes.c_char_p), i32]
+    lib.strata_status_str.restype = ctypes.c_char_p
+    lib.strata_status_str.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+EXPORTED_SYMBOLS = ("strata_moe_workspace_bytes", "strata_moe_route", "strata_moe_forward",
+                    "strata_moe_kernel_names", "strata_status_str")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(status: int):
+    if status != STRATA_OK:
+        msg = load_library().strata_status_str(status).decode()
+        raise StrataError(status, msg)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class LayerData:
+    """Device tensors of one layer (torch tensors or raw device addresses)."""
+    router_w: object
+    codes: object
+    scales: object
+    router_bias: object = None
+    resident_mask: object = None
+
+    def as_c(self) -> Layer:
+        return Layer(_ptr(self.router_w), _ptr(self.router_bias), _ptr(self.codes), _ptr(self.scales),
+                     _ptr(self.resident_mask))
+
+
+def shape(n_experts: int, top_k: int, d_model: int, d_ff: int, bits: int, n_shared: int = 1) -> Shape:
+    return Shape(n_experts, top_k, n_shared, d_model, d_ff, bits)
+
+
+def workspace_bytes(sh: Shape, T: int, L: int = 1) -> int:
+    n = load_library().strata_moe_workspace_bytes(ctypes.byref(sh), T, L)
+    if n == 0:
+        raise StrataError(STRATA_EINVAL, "unsupported shape")
+    return n
+
+
+def kernel_names(sh: Shape, T: int) -> list:
+    arr = (ctypes.c_char_p * 16)()
+    n = load_library().strata_moe_kernel_names(ctypes.byref(sh), T, arr, 16)
+    return [arr[i].decode() for i in range(n)]
+
+
+def _route_out(ro: Optional[dict]) -> Optional[RouteOut]:
+    if ro is None:
+        return None
+    return RouteOut(_ptr(ro.get("topk_idx")), _ptr(ro.get("topk_w")), _ptr(ro.get("counts")),
+                    _ptr(ro.get("offsets")), _ptr(ro.get("perm")), _ptr(ro.get("pos")))
+
+
+def route(sh: Shape, layer: LayerData, x, xdtype: int, T: int, out: dict, ws, ws_bytes: int, stream=None):
+    """Routing of one layer; `out` maps RouteOut field names to device tensors."""
+    lib = load_library()
+    ro = _route_out(out)
+    _check(lib.strata_moe_route(ctypes.byref(sh), ctypes.byref(layer.as_c()), _ptr(x), xdtype, T,
+                                ctypes.byref(ro) if ro is not None else None, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, ws, ws_bytes: int,
+            resid_out=None, route_outs: Optional[Sequence[dict]] = None, miss_te=None, miss_w=None,
+            miss_cap: int = 0, miss_count=None, flags: int = 0, events: Optional[Sequence[int]] = None,
+            stream=None):
+    """Forward of len(layers) stacked layers (see strata_moe_forward)."""
+    lib = load_library()
+    L = len(layers)
+    c_layers = (Layer * L)(*[ly.as_c() for ly in layers])
+    c_ro = None
+    if route_outs is not None:
+        assert len(route_outs) == L
+        c_ro = (RouteOut * L)(*[_route_out(r) or RouteOut() for r in route_outs])
+    ev = None
+    n_ev = 0
+    if events:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        n_ev = len(events) // 2
+    _check(lib.strata_moe_forward(ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last),
+                                  _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w), miss_cap, _ptr(miss_count),
+                                  _ptr(ws), ws_bytes, ev, n_ev, _stream(stream)))

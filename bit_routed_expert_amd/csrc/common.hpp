@@ -1,0 +1,128 @@
+// Device helpers and the internal launch interface of the MoE layer library.
+// gfx950 only (64-wide wavefronts).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace strata {
+
+constexpr int WAVE = 64;
+constexpr int CHUNK_TOK = 8;      // tokens one expert work item carries (GEMV path)
+constexpr int XPLANES = 4;        // base-16 digit planes of a layer input (16-bit fixed point)
+constexpr int HPLANES = 6;        // digit planes of the SwiGLU activation h (24-bit fixed point)
+constexpr float RMS_EPS = 1e-6f;
+
+// Largest |X| that P balanced base-16 digits in [-8, 7] represent symmetrically:
+// 7 * (16^P - 1) / 15.
+__host__ __device__ constexpr int digit_limit(int P) {
+    int s = 0, m = 1;
+    for (int i = 0; i < P; ++i) { s += m; m *= 16; }
+    return 7 * s;
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+template <typename T> __device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// Exponent E such that max_abs * 2^E fits the P-digit range, as large as possible.
+template <int P> __device__ __forceinline__ int fixed_point_exponent(float max_abs) {
+    if (!(max_abs > 0.f)) return 0;
+    int e;
+    frexpf(max_abs, &e);              // max_abs < 2^e
+    int E = 4 * P - 1 - e;            // max_abs * 2^E < 2^(4P-1)
+    if (ldexpf(max_abs, E) > (float)digit_limit(P)) E -= 1;
+    return E;
+}
+
+// Balanced base-16 digits of X (|X| <= digit_limit(P)), least significant first.
+template <int P> __device__ __forceinline__ void to_digits(int X, int d[P]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        int v = ((X + 8) & 15) - 8;
+        d[p] = v;
+        X = (X - v) >> 4;
+    }
+}
+
+// Work item of the expert kernels: up to CHUNK_TOK tokens of one expert.
+struct WorkItem {
+    int32_t expert;     // 0..E-1 routed, E shared
+    int32_t slot0;      // first slot; slots slot0 .. slot0+ntok-1
+    int32_t ntok;
+};
+
+// Everything the kernels of one layer call need; device pointers.
+struct LayerArgs {
+    // shape
+    int E, k, d, f, bits, T;
+    // layer data
+    const float *Wr;
+    const float *bias;
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint32_t *mask;
+    // input of this layer: residual stream x (bf16 or fp32) and whether to normalise it
+    const void *x;
+    int x_is_bf16;
+    int normalize;
+    // routing state (internal)
+    float *z;            // [T][E] logits
+    int32_t *idx;        // [T][k]
+    float *gate;         // [T][k]
+    int32_t *counts;     // [E]
+    int32_t *offsets;    // [E+1]
+    int32_t *perm;       // [T*k]
+    int32_t *pos;        // [T*k]
+    float *inv_rms;      // [T]
+    WorkItem *items;     // work list
+    int32_t *n_items;    // [1]
+    uint32_t *counter;   // self-resetting arrival counter
+    // optional user copies of routing
+    int32_t *u_idx;
+    float *u_gate;
+    int32_t *u_counts, *u_offsets, *u_perm, *u_pos;
+    // miss list
+    int32_t *miss_te;
+    float *miss_w;
+    int32_t miss_cap;
+    int32_t *miss_count;
+    // activation digit planes of the layer input: [T][d/32][XPLANES][4] words,
+    // per (token, 128-column group) digit sums, per (token, 256-column group) 2^-E
+    uint32_t *xq;
+    int32_t *xsum;
+    float *xscl;
+    // expert outputs
+    float *G, *U;        // [slots][f] gate and up projections
+    float *Y;            // [slots][d] expert outputs
+    // combine outputs
+    float *out;          // [T][d] layer output
+    float *x_next;       // [T][d] residual stream after this layer (nullable)
+    int route_only;
+};
+
+// Launchers (one file each); return hipGetLastError() of their launches.
+hipError_t launch_route_small(const LayerArgs &a, hipStream_t s);
+hipError_t launch_prep_x(const LayerArgs &a, hipStream_t s);
+hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
+hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
+hipError_t launch_route_permute(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gemv_gateup(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_gemv_down(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
+bool gemv_supported(int d, int f, int bits);
+
+}  // namespace strata

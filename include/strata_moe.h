@@ -1,0 +1,152 @@
+/*
+ * strata_moe.h -- C ABI of the MI355X (gfx950) sparse MoE layer forward.
+ *
+ * What one layer computes, per token t (E routed experts, top-k, 1 shared):
+ *   z[t][e]   = sum_i Wr[e][i] * u[t][i] (+ bias[e])              fp32 router logits
+ *   idx[t][r] = the k experts with the largest z, ordered by (z desc, e asc)
+ *   gate[t][r]= softmax over all E, renormalised over the k picked (fp32)
+ *   per expert e:  h = silu(Wg_e u) * (Wu_e u),  y_e = Wd_e h          (SwiGLU)
+ *   out[t]    = y_shared[t] + sum_{r<k, e=idx[t][r] resident} gate[t][r] * y_e[t]
+ * The structure (512 routed experts per layer, 10 routed + 1 shared per
+ * token per layer, 48 layers) is the model the pages describe:
+ * greenbean-ai, "Strata 如何讓 12GB 顯卡跑 Qwen3.8-Flash-Next？", section 一;
+ * wiselychen.com, "Strata ... RTX 5090 ... 1M context", "30 秒定位" table.
+ * Experts that are not resident on the accelerator are computed elsewhere
+ * (same page, technique 2 "專家快取與 CPU／GPU 分工"; greenbean-ai section 二;
+ * tutuge.me "⚙️ 125B 是怎么塞进游戏 PC 的"): here a resident mask drops them
+ * from the GPU sum and lists them, with their gates, in a miss list.
+ *
+ * Stacks of L layers (an MTP verify step runs the drafted tokens through all
+ * layers in one batch: wiselychen.com technique 4 "MTP 推測解碼";
+ * greenbean-ai section 三): x_0 = x; layer l consumes u_l = x_0 for l = 0
+ * (or rmsnorm(x_0) with STRATA_NORM_FIRST) and u_l = rmsnorm(x_l) for
+ * l > 0, where rmsnorm(v) = v / sqrt(mean(v^2) + 1e-6) (no learnt gain);
+ * x_{l+1} = x_l + out_l in fp32.
+ *
+ * WEIGHT FORMAT (the pages name ~3-bit IQ3_XXS at about 3.06 bit/weight,
+ * wiselychen.com technique 1 "低位元量化", and 2-bit Q2_0, greenbean-ai section
+ * 四, but give no byte layout; this library fixes one):
+ *   w = fp16 scale of its 256-element block * (code - c0),
+ *   3-bit codes 0..7 with c0 = 3.5 (3.0625 bit/weight with the scale),
+ *   2-bit codes 0..3 with c0 = 1.5 (2.0625 bit/weight).
+ *   Per expert: gate [f][d], up [f][d], down [d][f] (out x in, row-major),
+ *   experts 0..E-1 routed, then the shared expert E.  Requirements:
+ *   d % 128 == 0 and f % 128 == 0.
+ *   codes: element (r, c) of a matrix [out][in] sits in a 32-column "unit"
+ *     at byte offset (((r/16)*(in/128) + c/128)*16 + r%16)*4*UB + ((c%128)/32)*UB
+ *     (UB = 12 for 3-bit, 8 for 2-bit) at place j = c % 32.
+ *     3-bit unit = little-endian u32 words A, B, C:
+ *       j < 24 : code = bits [4n, 4n+3) of (A, B, C)[j/8], n = j % 8;
+ *       j >= 24: n = j-24, code = A bit(4n+3) | B bit(4n+3)<<1 | C bit(4n+3)<<2.
+ *     2-bit unit = little-endian u32 words A (j < 16), B (j >= 16):
+ *       jj = j % 16: code = bits [4(jj%8) + 2(jj/8), +2) of the word.
+ *     Matrix m of expert e starts at byte (3e + m) * d*f*bits/8.
+ *   scales: IEEE binary16, one per 256 consecutive elements of the
+ *     row-major flattened matrix: index (3e + m) * (d*f/256) + (r*in + c)/256.
+ *
+ * CONVENTIONS
+ *   Pointers marked [dev] are device pointers, [host] host pointers.  The
+ *   caller owns every buffer, including the workspace; the library never
+ *   allocates on these entry points and keeps no per-call global state.
+ *   Calls enqueue on `stream` (a hipStream_t, passed as void*) and return
+ *   without a host synchronisation; outputs are valid once the stream is
+ *   synchronised.  Validation happens on the host before any launch and
+ *   nothing is enqueued when it fails.  Calls that overlap on one workspace
+ *   race.
+ *   The workspace must be zero-filled before its first use; every call
+ *   leaves its internal counters at zero again.
+ */
+#ifndef STRATA_MOE_H
+#define STRATA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STRATA_OK = 0,
+    STRATA_EINVAL = 1,       /* null required pointer or inconsistent argument */
+    STRATA_EUNSUPPORTED = 2, /* shape or format this build does not handle */
+    STRATA_EWORKSPACE = 3,   /* workspace smaller than strata_moe_workspace_bytes() */
+    STRATA_EHIP = 4          /* a HIP launch failed; strata_status_str() names it */
+} strata_status;
+
+typedef enum { STRATA_X_BF16 = 0, STRATA_X_F32 = 1 } strata_xdtype;
+
+enum { STRATA_NORM_FIRST = 1u }; /* forward flags: rmsnorm the first layer's input too */
+
+/* [host] layer shape.  bits = 3 or 2.  n_shared must be 1.
+ * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 1024. */
+typedef struct {
+    int32_t n_experts, top_k, n_shared, d_model, d_ff, bits;
+} strata_moe_shape;
+
+/* [host] struct of [dev] pointers, one per layer. */
+typedef struct {
+    const float *router_w;          /* [E][d] fp32 */
+    const float *router_bias;       /* [E] fp32, or NULL */
+    const uint8_t *codes;           /* (E+1) experts, format above */
+    const uint16_t *scales;         /* (E+1) experts, fp16 bit patterns */
+    const uint32_t *resident_mask;  /* [ceil(E/32)] bitset (bit e%32 of word e/32), or NULL = all resident */
+} strata_moe_layer;
+
+/* [host] struct of optional [dev] outputs (any field may be NULL):
+ *   topk_idx [T][k] int32, topk_w [T][k] fp32 (gates),
+ *   counts [E] int32 (routed picks per expert), offsets [E+1] int32 (exclusive prefix sum),
+ *   perm [T*k] int32: slot -> t*k + r, slots ordered by (expert asc, token asc),
+ *   pos  [T*k] int32: t*k + r -> slot. */
+typedef struct {
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *pos;
+} strata_route_out;
+
+/* Bytes of workspace a call with this shape, T tokens and L layers needs. */
+size_t strata_moe_workspace_bytes(const strata_moe_shape *shape, int32_t T, int32_t L);
+
+/* Routing only (the router, top-k, gates and permutation of one layer) for
+ * T tokens x [dev] [T][d] (bf16 or fp32) used as given.
+ * T = 0 is a no-op returning STRATA_OK. */
+strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_layer *layer, const void *x,
+                               strata_xdtype xdtype, int32_t T, const strata_route_out *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* Forward of L stacked layers for T tokens.
+ *   layers     [host] array of L layer structs.
+ *   x          [dev] [T][d] bf16 or fp32, the first layer's residual stream x_0.
+ *   flags      STRATA_NORM_FIRST or 0.
+ *   y_last     [dev] [T][d] fp32: out of the last layer (required).
+ *   resid_out  [dev] [T][d] fp32: x_L (nullable).
+ *   route_out  [host] array of L structs (nullable): routing of each layer.
+ *   miss_te    [dev] [miss_cap][2] int32 (t, e); miss_w [dev] [miss_cap] fp32 gates;
+ *   miss_count [dev] [L] int32: true number of misses per layer.  The first
+ *              miss_cap misses of each layer, in (t asc, r asc) order, are written at
+ *              miss_te + l*miss_cap*2 / miss_w + l*miss_cap.  The miss buffers may be
+ *              NULL only when no layer has a resident mask; miss_cap = T*k never overflows.
+ *   events     [host] array of 2*n_events hipEvent_t (as void*) or NULL: when given, the
+ *              library records events[2i] before and events[2i+1] after the i-th kernel
+ *              it enqueues (i < n_events), for per-kernel timing by the caller.
+ * T = 0 is a no-op returning STRATA_OK. */
+strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
+                                 const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
+                                 float *resid_out, const strata_route_out *route_out, int32_t *miss_te,
+                                 float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws, size_t ws_bytes,
+                                 void *const *events, int32_t n_events, void *stream);
+
+/* Names of the kernels strata_moe_forward enqueues for one layer, in order,
+ * for a token count T; returns how many (<= max) and writes static strings. */
+int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max);
+
+/* Static description of a status (for STRATA_EHIP, of the last HIP error). */
+const char *strata_status_str(strata_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRATA_MOE_H */

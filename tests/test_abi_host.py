@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI that need no GPU: every declared symbol is
+exported, workspace sizing, and the validation errors (nothing is launched
+when validation fails)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_routed_expert_amd as brx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "strata_moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(strata_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = brx.load_library()
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(brx.EXPORTED_SYMBOLS)
+
+
+def test_workspace_sizes():
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    assert brx.workspace_bytes(sh, 1) > 0
+    assert brx.workspace_bytes(sh, 4096) > brx.workspace_bytes(sh, 5)
+    # expert outputs dominate: (T*k + T) slots x (d + 2f) fp32
+    assert brx.workspace_bytes(sh, 4096) >= 4096 * 11 * (2048 + 2 * 768) * 4
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_shared=0), dict(top_k=0), dict(top_k=33), dict(n_experts=5, top_k=10), dict(d_model=200),
+    dict(d_ff=100), dict(n_experts=2048)])
+def test_invalid_shapes_rejected(bad):
+    kw = dict(n_experts=512, top_k=10, n_shared=1, d_model=2048, d_ff=768, bits=3)
+    kw.update(bad)
+    sh = brx.Shape(kw["n_experts"], kw["top_k"], kw["n_shared"], kw["d_model"], kw["d_ff"], kw["bits"])
+    lib = brx.load_library()
+    assert lib.strata_moe_workspace_bytes(ctypes.byref(sh), 1, 1) == 0
+    st = lib.strata_moe_forward(ctypes.byref(sh), None, 1, None, 0, 1, 0, None, None, None, None, None, 0, None,
+                                None, 0, None, 0, None)
+    assert st == brx.STRATA_EINVAL
+
+
+def test_unsupported_bits():
+    sh = brx.shape(512, 10, 2048, 768, 4)
+    lib = brx.load_library()
+    st = lib.strata_moe_forward(ctypes.byref(sh), None, 1, None, 0, 1, 0, None, None, None, None, None, 0, None,
+                                None, 0, None, 0, None)
+    assert st == brx.STRATA_EUNSUPPORTED
+
+
+def _fake_layer():
+    # non-null placeholders: validation fails before anything touches them
+    return brx.Layer(0x1000, None, 0x2000, 0x3000, None)
+
+
+def test_forward_validation_errors():
+    lib = brx.load_library()
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    ly = (brx.Layer * 1)(_fake_layer())
+    need = brx.workspace_bytes(sh, 4)
+
+    def call(**kw):
+        a = dict(layers=ly, L=1, x=0x4000, xd=0, T=4, flags=0, y=0x5000, ws=0x6000, wsb=need, cap=0, mte=None,
+                 mw=None, mc=None, nev=0, ev=None)
+        a.update(kw)
+        return lib.strata_moe_forward(ctypes.byref(sh), a["layers"], a["L"], a["x"], a["xd"], a["T"], a["flags"],
+                                      a["y"], None, None, a["mte"], a["mw"], a["cap"], a["mc"], a["ws"], a["wsb"],
+                                      a["ev"], a["nev"], None)
+
+    assert call(T=-1) == brx.STRATA_EINVAL
+    assert call(T=0, x=None, y=None, ws=None) == brx.STRATA_OK          # T = 0 is a no-op
+    assert call(L=0) == brx.STRATA_EINVAL
+    assert call(x=None) == brx.STRATA_EINVAL
+    assert call(y=None) == brx.STRATA_EINVAL
+    assert call(ws=None) == brx.STRATA_EINVAL
+    assert call(xd=7) == brx.STRATA_EINVAL
+    assert call(flags=8) == brx.STRATA_EINVAL
+    assert call(cap=-1) == brx.STRATA_EINVAL
+    assert call(nev=2) == brx.STRATA_EINVAL
+    assert call(wsb=need - 1) == brx.STRATA_EWORKSPACE
+    masked = (brx.Layer * 1)(brx.Layer(0x1000, None, 0x2000, 0x3000, 0x7000))
+    assert call(layers=masked) == brx.STRATA_EINVAL                   # mask needs miss buffers
+    nocodes = (brx.Layer * 1)(brx.Layer(0x1000, None, None, 0x3000, None))
+    assert call(layers=nocodes) == brx.STRATA_EINVAL
+
+
+def test_route_validation_errors():
+    lib = brx.load_library()
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    ly = _fake_layer()
+    need = brx.workspace_bytes(sh, 4)
+    f = lib.strata_moe_route
+    assert f(ctypes.byref(sh), ctypes.byref(ly), 0x4000, 0, -1, None, 0x6000, need, None) == brx.STRATA_EINVAL
+    assert f(ctypes.byref(sh), ctypes.byref(ly), 0x4000, 0, 0, None, 0x6000, need, None) == brx.STRATA_OK
+    assert f(ctypes.byref(sh), ctypes.byref(ly), None, 0, 4, None, 0x6000, need, None) == brx.STRATA_EINVAL
+    assert f(ctypes.byref(sh), ctypes.byref(ly), 0x4000, 0, 4, None, 0x6000, need - 8, None) == \
+        brx.STRATA_EWORKSPACE
+
+
+def test_status_strings():
+    lib = brx.load_library()
+    for s in range(4):
+        assert lib.strata_status_str(s)
+
+
+def test_kernel_names_by_path():
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    assert brx.kernel_names(sh, 1)[0] == "route_small"
+    assert "route_permute" in brx.kernel_names(sh, 4096)

@@ -1,0 +1,124 @@
+"""Parity of the HIP path (called through the C ABI) with the oracle.
+
+Integers (top-k ids, counts, offsets, permutation, miss list) bit-exact;
+gates within 1e-6; float outputs within max-abs 2e-3 x RMS of the oracle's
+output over the compared tensor.  Inputs are drawn with top-(k+1) logit
+margins >= 1e-3 so the ordered routing is unique.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+from tests import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_case(name, T=None, rep=0, with_mask=None, bits=None):
+    w = synth.WORKLOADS[name]
+    if bits is not None and bits != w.bits:
+        w = synth.Workload(w.name + f"_b{bits}", w.n_experts, w.top_k, w.d_model, w.d_ff, bits, w.tokens,
+                           seed=w.seed + 0x100)
+    T = T or w.tokens_per_call
+    L = W.layer_data(w, 0)
+    if with_mask is not None:
+        L["mask"] = with_mask
+    x, _ = W.draw_tokens(w, L["Wr"], L["bias"], range(T), rep=rep)
+    return w, L, x, T
+
+
+def _oracle_layer(w, L, u, mask=None):
+    return oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, L["Wr"], L["codes"],
+                            L["scales"], bias=L["bias"], mask=mask if mask is not None else L.get("mask"))
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_tiny_layer(bits):
+    w, L, x, T = _layer_case("tiny", bits=bits)
+    print(f"case tiny bits={bits} T={T}", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    np.testing.assert_array_equal(got["resid"], (synth.bf16_to_f32(x) + got["y"]).astype(np.float32))
+
+
+def test_tiny_layer_with_mask_and_misses():
+    mask = np.array([0b0110_1011_1001_0111], np.uint32)
+    w, L, x, T = _layer_case("tiny", with_mask=mask)
+    print(f"case tiny masked T={T}", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    n = int(got["miss_count"][0])
+    assert n == ref["miss_count"]
+    np.testing.assert_array_equal(got["miss_te"][0][:n], ref["miss_te"])
+    assert np.max(np.abs(got["miss_w"][0][:n] - ref["miss_w"]), initial=0) <= G.GATE_TOL
+
+
+def test_tiny_miss_list_overflow_keeps_true_count():
+    mask = np.array([0b0000_0000_0000_0001], np.uint32)      # only expert 0 resident
+    w, L, x, T = _layer_case("tiny", with_mask=mask)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T, miss_cap=3)
+    assert int(got["miss_count"][0]) == ref["miss_count"] > 3
+    np.testing.assert_array_equal(got["miss_te"][0][:3], ref["miss_te"][:3])
+
+
+def test_decode_layer_full_size():
+    w, L, x, T = _layer_case("decode")
+    print("case decode T=1", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    r = G.assert_close(got["y"], ref["out"])
+    print(f"decode max-abs/RMS {r:.2e}")
+
+
+def test_verify_batch_five_tokens_and_batch_invariance():
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 0)
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(5), rep=3)
+    print("case T=5 one layer", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    dl = [G.layer_to_dev(L)]
+    got = G.run_forward(w, dl, G.dev(x), 0, 5)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    # the verify batch equals token-by-token evaluation, bit for bit
+    for t in range(5):
+        one = G.run_forward(w, dl, G.dev(x[t:t + 1]), 0, 1, want_route=False)
+        np.testing.assert_array_equal(one["y"][0], got["y"][t])
+
+
+def test_decode_repeat_is_bitwise_identical():
+    w, L, x, T = _layer_case("decode", rep=5)
+    dl = [G.layer_to_dev(L)]
+    a = G.run_forward(w, dl, G.dev(x), 0, T)
+    b = G.run_forward(w, dl, G.dev(x), 0, T)
+    np.testing.assert_array_equal(a["y"], b["y"])
+
+
+def test_fp32_input_with_norm_first():
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 0)
+    rng = np.random.default_rng(11)
+    # fp32 residual-stream input of a later layer: redraw rows until the margins hold
+    xs = []
+    while len(xs) < 3:
+        xr = (7.0 * rng.standard_normal(w.d_model)).astype(np.float32)
+        u = oracle.rmsnorm(xr[None])
+        if oracle.topk_margin(oracle.logits(u, L["Wr"]), w.top_k)[0] >= W.MARGIN:
+            xs.append(xr)
+    x = np.stack(xs)
+    u = oracle.rmsnorm(x)
+    ref = _oracle_layer(w, L, u)
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 1, 3, flags=1)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    np.testing.assert_array_equal(got["resid"], (x + got["y"]).astype(np.float32))
