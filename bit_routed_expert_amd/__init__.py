@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m bit_routed_expert_amd.build`")
+    try:  # bind to the HIP runtime torch has loaded (same SONAME), so streams are shared
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.strata_moe_workspace_bytes.restype = sz

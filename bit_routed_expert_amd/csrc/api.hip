@@ -3,7 +3,7 @@
 // Nothing here allocates device memory or synchronises the stream.
 #include <string.h>
 
-#include "../../include/strata_moe.h"
+#include "strata_moe.h"
 #include "common.hpp"
 
 using namespace strata;
@@ -19,8 +19,8 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr int SMALL_T = 8;
 
 struct Layout {
-    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, G, U, Y,
-        out, xres0, xres1, miss_count, total;
+    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hq, hsum,
+        hscl, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -48,10 +48,11 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.items = take(sizeof(WorkItem) * l.max_items);
     l.n_items = take(4);
     l.xq = take((size_t)T * (d / 32) * XPLANES * 16);
-    l.xsum = take(4 * T * (d / 128));
+    l.xsum = take(4 * T * (d / 32));
     l.xscl = take(4 * T * ((d + 255) / 256));
-    l.G = take(sizeof(float) * slots * f);
-    l.U = take(sizeof(float) * slots * f);
+    l.hq = take((size_t)slots * (f / 32) * XPLANES * 16);
+    l.hsum = take(4 * slots * (f / 32));
+    l.hscl = take(4 * slots * (f / 32));
     l.Y = take(sizeof(float) * slots * d);
     l.out = take(sizeof(float) * T * d);
     l.xres0 = take(sizeof(float) * T * d);
@@ -97,8 +98,9 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xq = (uint32_t *)(ws + l.xq);
     a.xsum = (int32_t *)(ws + l.xsum);
     a.xscl = (float *)(ws + l.xscl);
-    a.G = (float *)(ws + l.G);
-    a.U = (float *)(ws + l.U);
+    a.hq = (uint32_t *)(ws + l.hq);
+    a.hsum = (int32_t *)(ws + l.hsum);
+    a.hscl = (float *)(ws + l.hscl);
     a.Y = (float *)(ws + l.Y);
 }
 
@@ -136,10 +138,13 @@ struct Recorder {
         }                                           \
     } while (0)
 
-// Route (and, unless route_only, prepare the input digit planes) of one layer.
+// Route (and, unless route_only, prepare the input digit planes) of one
+// layer.  On the decode path the top-k is taken inside the gate/up kernel
+// (forward) or by a one-block finisher (routing only).
 strata_status route_layer(LayerArgs &a, const strata_moe_shape &s, int T, Recorder &rec) {
     if (small_path(s, T)) {
-        RUN(launch_route_small(a, rec.s));
+        RUN(launch_route_logits_small(a, rec.s));
+        if (a.route_only) RUN(launch_route_small_finish(a, rec.s));
     } else {
         RUN(launch_prep_x(a, rec.s));
         RUN(launch_route_logits(a, rec.s));
@@ -171,13 +176,15 @@ const char *strata_status_str(strata_status s) {
 }
 
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max) {
-    static const char *small[] = {"route_small", "gemv_gateup", "gemv_down", "combine"};
+    static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
+    static const char *small4[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
     static const char *large[] = {"prep_x", "route_logits", "route_topk", "route_permute",
                                   "gemv_gateup", "gemv_down", "combine"};
     if (check_shape(shape) != STRATA_OK) return 0;
     const bool sp = small_path(*shape, T);
-    const char **src = sp ? small : large;
-    const int n = sp ? 4 : 7;
+    const bool rows = sp && down_rows_fits(T, shape->top_k, shape->d_ff);
+    const char **src = sp ? (rows ? small : small4) : large;
+    const int n = sp ? (rows ? 3 : 4) : 7;
     for (int i = 0; i < n && i < max; ++i) names[i] = src[i];
     return n;
 }
@@ -258,9 +265,19 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         a.x_next = (l == L - 1) ? resid_out : (float *)(w + (l % 2 ? lay.xres1 : lay.xres0));
         st = route_layer(a, *shape, T, rec);
         if (st != STRATA_OK) return st;
-        RUN(launch_gemv_gateup(a, (int)lay.max_items, rec.s));
-        RUN(launch_gemv_down(a, (int)lay.max_items, rec.s));
-        RUN(launch_combine(a, rec.s));
+        if (small_path(*shape, T)) {
+            RUN(launch_gemv_gateup_small(a, (int)lay.max_items, rec.s));
+            if (down_rows_fits(T, shape->top_k, shape->d_ff)) {
+                RUN(launch_gemv_down_rows(a, rec.s));
+            } else {
+                RUN(launch_gemv_down(a, (int)lay.max_items, rec.s));
+                RUN(launch_combine(a, rec.s));
+            }
+        } else {
+            RUN(launch_gemv_gateup(a, (int)lay.max_items, rec.s));
+            RUN(launch_gemv_down(a, (int)lay.max_items, rec.s));
+            RUN(launch_combine(a, rec.s));
+        }
     }
     return STRATA_OK;
 }

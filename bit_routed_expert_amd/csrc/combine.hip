@@ -12,18 +12,36 @@
 
 namespace strata {
 
+constexpr int KMAX = 32;
+
 template <int XBF16>
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int d = a.d, k = a.k, T = a.T;
     if (gid >= (int64_t)T * d) return;
     const int t = (int)(gid / d), i = (int)(gid % d);
-    float s = a.Y[((int64_t)T * k + t) * d + i];
-    for (int r = 0; r < k; ++r) {
-        const int e = a.idx[t * k + r];
-        if (a.mask && !((a.mask[e >> 5] >> (e & 31)) & 1u)) continue;
-        s = fmaf(a.gate[t * k + r], a.Y[(int64_t)a.pos[t * k + r] * d + i], s);
+    const float *__restrict__ Y = a.Y;
+    // all routing reads first (independent loads), then all expert rows
+    int pr[KMAX];
+    float gr[KMAX];
+    bool on[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+        if (r < k) {
+            const int e = a.idx[t * k + r];
+            pr[r] = a.pos[t * k + r];
+            gr[r] = a.gate[t * k + r];
+            on[r] = !a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u);
+        }
     }
+    float s = Y[((int64_t)T * k + t) * d + i];
+    float yv[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+        if (r < k) yv[r] = on[r] ? Y[(int64_t)pr[r] * d + i] : 0.f;
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+        if (r < k && on[r]) s = fmaf(gr[r], yv[r], s);
     a.out[gid] = s;
     if (a.x_next) {
         const float xv = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[gid]) : ((const float *)a.x)[gid];

@@ -8,8 +8,7 @@ namespace strata {
 
 constexpr int WAVE = 64;
 constexpr int CHUNK_TOK = 8;      // tokens one expert work item carries (GEMV path)
-constexpr int XPLANES = 4;        // base-16 digit planes of a layer input (16-bit fixed point)
-constexpr int HPLANES = 6;        // digit planes of the SwiGLU activation h (24-bit fixed point)
+constexpr int XPLANES = 6;        // base-16 digit planes of an activation (24-bit fixed point)
 constexpr float RMS_EPS = 1e-6f;
 
 // Largest |X| that P balanced base-16 digits in [-8, 7] represent symmetrically:
@@ -100,14 +99,17 @@ struct LayerArgs {
     float *miss_w;
     int32_t miss_cap;
     int32_t *miss_count;
-    // activation digit planes of the layer input: [T][d/32][XPLANES][4] words,
-    // per (token, 128-column group) digit sums, per (token, 256-column group) 2^-E
+    // digit planes of the layer input: [T][d/32][XPLANES][4] words, per
+    // (token, 32-column unit) digit sums, per (token, 256-column group) 2^-E
     uint32_t *xq;
     int32_t *xsum;
     float *xscl;
-    // expert outputs
-    float *G, *U;        // [slots][f] gate and up projections
-    float *Y;            // [slots][d] expert outputs
+    // SwiGLU activation h of each slot, quantised per 32-column unit:
+    // [slots][f/32][XPLANES][4] words, per-unit digit sums and 2^-E
+    uint32_t *hq;
+    int32_t *hsum;
+    float *hscl;
+    float *Y;            // [slots][d] expert outputs (larger T)
     // combine outputs
     float *out;          // [T][d] layer output
     float *x_next;       // [T][d] residual stream after this layer (nullable)
@@ -115,13 +117,17 @@ struct LayerArgs {
 };
 
 // Launchers (one file each); return hipGetLastError() of their launches.
-hipError_t launch_route_small(const LayerArgs &a, hipStream_t s);
+hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);
+hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_prep_x(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_permute(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemv_gateup(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemv_down(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_gemv_down_rows(const LayerArgs &a, hipStream_t s);
+bool down_rows_fits(int T, int k, int f);
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
 bool gemv_supported(int d, int f, int bits);
 

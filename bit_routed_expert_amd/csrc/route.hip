@@ -7,57 +7,13 @@
 // Qwen3.8-Flash-Next？", section 一); the GPU runs the router (same page,
 // section 二).  Logits are fp32; top-k is ordered by (logit desc, index asc);
 // gates are the softmax renormalised over the k picks.
-#include "common.hpp"
+#include "routing.hpp"
 
 namespace strata {
 
-// ----------------------------------------------------------------- top-k
-// One wave picks the top-k of E logits (z already scaled and biased) and
-// writes ordered ids and gates.  Lane l owns experts l, l+64, ...
-__device__ void wave_topk(const float *z, int E, int k, int32_t *idx_out, float *gate_out, int32_t *idx_out2,
-                          float *gate_out2) {
-    const int lane = threadIdx.x & 63;
-    constexpr int JM = 16;  // E <= 1024
-    float v[JM];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        int e = lane + 64 * j;
-        v[j] = (e < E) ? z[e] : -INFINITY;
-        if (e >= E) taken |= 1u << j;
-    }
-    float selz0 = 0.f, myz = 0.f;
-    int mye = 0;
-    for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < JM; ++j) {
-            int e = lane + 64 * j;
-            bool ok = !((taken >> j) & 1u);
-            if (ok && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, WAVE);
-            int oe = __shfl_xor(be, o, WAVE);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (r == 0) selz0 = bv;
-        if (lane == r) { myz = bv; mye = be; }
-    }
-    // gates: softmax over the k picks (the all-E normaliser cancels in the renormalisation)
-    float p = (lane < k) ? expf(myz - selz0) : 0.f;
-    float s = wave_sum(p);
-    if (lane < k) {
-        float g = p / s;
-        idx_out[lane] = mye;
-        gate_out[lane] = g;
-        if (idx_out2) idx_out2[lane] = mye;
-        if (gate_out2) gate_out2[lane] = g;
-    }
-}
+// Every kernel here stays within the 64 KiB of LDS a block gets by default;
+// a launch that would need more is refused rather than attempted.
+constexpr size_t LDS_LIMIT = 64 * 1024;
 
 // ------------------------------------------------------ input digit planes
 // For token t: inverse RMS (or 1) and the digit planes of u = x * inv_rms:
@@ -108,15 +64,15 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
 #pragma unroll
             for (int p = 0; p < XPLANES; ++p) word[p] |= ((uint32_t)dg[p] & 15u) << (4 * n);
         }
-        // digit sums per 128-column group (16 consecutive chunks)
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) sx += __shfl_xor(sx, o, WAVE);
+        // digit sums per 32-column unit (4 consecutive chunks)
+        sx += __shfl_xor(sx, 1, WAVE);
+        sx += __shfl_xor(sx, 2, WAVE);
         if (valid) {
             int U = c / 4, i = c % 4;
             uint32_t *dst = a.xq + ((size_t)t * (d / 32) + U) * (XPLANES * 4);
 #pragma unroll
             for (int p = 0; p < XPLANES; ++p) dst[p * 4 + i] = word[p];
-            if ((c & 15) == 0) a.xsum[(size_t)t * (d / 128) + c / 16] = sx;
+            if (i == 0) a.xsum[(size_t)t * (d / 32) + U] = sx;
             if ((c & 31) == 0) a.xscl[(size_t)t * G + c / 32] = ldexpf(1.f, -E);
         }
     }
@@ -128,10 +84,15 @@ __device__ float token_inv_rms(const LayerArgs &a, int t, float *red) {
     if (!a.normalize) return 1.f;
     const int d = a.d, nth = blockDim.x, th = threadIdx.x;
     float ss = 0.f;
-    for (int i = th; i < d; i += nth) {
-        size_t o = (size_t)t * d + i;
-        float xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
-        ss += xv * xv;
+    for (int i0 = 0; i0 < d; i0 += 8 * nth) {  // 8 independent loads in flight per pass
+        float xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const size_t o = (size_t)t * d + min(i0 + th + j * nth, d - 1);
+            xv[j] = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += (i0 + th + j * nth < d) ? xv[j] * xv[j] : 0.f;
     }
     ss = wave_sum(ss);
     __syncthreads();
@@ -143,170 +104,70 @@ __device__ float token_inv_rms(const LayerArgs &a, int t, float *red) {
     return 1.f / sqrtf(tot / (float)d + RMS_EPS);
 }
 
-__device__ __forceinline__ bool is_resident(const uint32_t *mask, int e) {
-    return !mask || ((mask[e >> 5] >> (e & 31)) & 1u);
-}
-
-// --------------------------------------------- small-T permutation & lists
-// One block; T*k <= blockDim.x.  Stable permutation (expert asc, token asc),
-// work list (one item per resident expert with picks, then the shared expert
-// in items of <= CHUNK_TOK tokens), miss list in (t, r) order.
-__device__ void small_permute(const LayerArgs &a, int32_t *lds /* >= 2E+2+blockDim ints */) {
-    const int th = threadIdx.x, nth = blockDim.x;
-    const int E = a.E, n = a.T * a.k;
-    int32_t *hist = lds;           // [E]
-    int32_t *offs = lds + E;       // [E+1]
-    int32_t *scan = lds + 2 * E + 1;  // [nth]
-    for (int e = th; e < E; e += nth) hist[e] = 0;
-    __syncthreads();
-    int my_e = -1;
-    if (th < n) {
-        my_e = a.idx[th];
-        atomicAdd(&hist[my_e], 1);
-    }
-    __syncthreads();
-    if (th == 0) {
-        int acc = 0;
-        for (int e = 0; e < E; ++e) { offs[e] = acc; acc += hist[e]; }
-        offs[E] = acc;
-    }
-    __syncthreads();
-    for (int e = th; e < E; e += nth) {
-        a.counts[e] = hist[e];
-        a.offsets[e] = offs[e];
-        if (a.u_counts) a.u_counts[e] = hist[e];
-        if (a.u_offsets) a.u_offsets[e] = offs[e];
-    }
-    if (th == 0) {
-        a.offsets[E] = offs[E];
-        if (a.u_offsets) a.u_offsets[E] = offs[E];
-    }
-    if (th < n) {
-        int t = th / a.k;
-        int rank = 0;
-        for (int j = 0; j < n; ++j)
-            if (j / a.k < t && a.idx[j] == my_e) ++rank;
-        int slot = offs[my_e] + rank;
-        a.perm[slot] = th;
-        a.pos[th] = slot;
-        if (a.u_perm) a.u_perm[slot] = th;
-        if (a.u_pos) a.u_pos[th] = slot;
-    }
-    // miss list: exclusive scan of non-resident flags in (t, r) order
-    int miss = (th < n && !is_resident(a.mask, my_e)) ? 1 : 0;
-    scan[th] = miss;
-    __syncthreads();
-    if (th == 0) {
-        int acc = 0;
-        for (int i = 0; i < nth; ++i) { int v = scan[i]; scan[i] = acc; acc += v; }
-        if (a.miss_count) *a.miss_count = acc;
-    }
-    __syncthreads();
-    if (miss && a.miss_te) {
-        int p = scan[th];
-        if (p < a.miss_cap) {
-            a.miss_te[2 * p] = th / a.k;
-            a.miss_te[2 * p + 1] = my_e;
-            a.miss_w[p] = a.gate[th];
-        }
-    }
-    __syncthreads();
-    // work list
-    if (th == 0) {
-        int ni = 0;
-        for (int e = 0; e < E; ++e)
-            if (hist[e] > 0 && is_resident(a.mask, e)) {
-                a.items[ni++] = WorkItem{e, offs[e], hist[e]};
-            }
-        for (int t0 = 0; t0 < a.T; t0 += CHUNK_TOK)
-            a.items[ni++] = WorkItem{E, n + t0, min(CHUNK_TOK, a.T - t0)};
-        *a.n_items = ni;
-    }
-}
 
 // ------------------------------------------------------ decode-size route
-// T <= 8.  Every block computes unnormalised logits of 8 experts (two per
-// wave) for all T tokens; the last block to arrive scales them by the
-// token's inverse RMS, adds the bias, picks the top-k, builds the
-// permutation and lists, and writes the input digit planes.
-constexpr int RS_EPB = 8;
-
-// LDS floats of route_small: x rows, or logits + reduction scratch, or the
-// permutation scratch, plus 4 words for the arrival flag.
-__host__ __device__ inline int small_lds_floats(const LayerArgs &a) {
-    int n = a.T * a.d;
-    n = n > 64 + a.E ? n : 64 + a.E;
-    n = n > 2 * a.E + 1 + 256 ? n : 2 * a.E + 1 + 256;
-    return n + 4;
-}
-
-template <typename K> static void allow_lds(K kernel, size_t bytes) {
-    if (bytes > 64 * 1024)
-        (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
+// T <= 8.  Blocks [0, ceil(E/4)): one router row per wave, its loads issued
+// before anything else, dotted with the T token rows staged in LDS; the
+// unnormalised logits go to z.  Blocks past those: one per token, its
+// inverse RMS and (unless routing only) its input digit planes.  The top-k
+// is taken later by every consumer block from z (a few KB), so no block
+// waits on another inside this kernel.
+constexpr int RS_WAVES = 4;   // router rows per block
+constexpr int RS_MAXJ = 8;    // float4 per lane per 2048-column chunk
 
 template <int XBF16>
-__global__ __launch_bounds__(256) void route_small_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
     extern __shared__ float lds[];
     const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
     const int d = a.d, T = a.T, E = a.E;
-    float *xs = lds;  // [T][d]
-    for (int i = th; i < T * d; i += 256)
-        xs[i] = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
-    __syncthreads();
-    for (int j = 0; j < RS_EPB / 4; ++j) {
-        int e = blockIdx.x * RS_EPB + wave * (RS_EPB / 4) + j;
-        if (e >= E) break;
-        const float *w = a.Wr + (size_t)e * d;
-        float acc[CHUNK_TOK];
-#pragma unroll
-        for (int t = 0; t < CHUNK_TOK; ++t) acc[t] = 0.f;
-        for (int i = lane * 4; i < d; i += 256) {
-            float4 wv = *(const float4 *)(w + i);
-#pragma unroll
-            for (int t = 0; t < CHUNK_TOK; ++t)
-                if (t < T) {
-                    const float *xr = xs + t * d + i;
-                    acc[t] += wv.x * xr[0] + wv.y * xr[1] + wv.z * xr[2] + wv.w * xr[3];
-                }
-        }
-#pragma unroll
-        for (int t = 0; t < CHUNK_TOK; ++t)
-            if (t < T) {
-                float s = wave_sum(acc[t]);
-                if (lane == 0) a.z[t * E + e] = s;
-            }
-    }
-    // arrival: the flag lives just past the largest LDS use
-    int &is_last = *(int *)(lds + small_lds_floats(a) - 4);
-    __threadfence();
-    __syncthreads();
-    if (th == 0) is_last = (atomicAdd(a.counter, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    if (th == 0) *a.counter = 0;
-
-    float *red = lds;  // reuse
-    float *zs = lds + 64;  // [E] per token in turn
-    for (int t = 0; t < T; ++t) {
-        float inv = token_inv_rms(a, t, red);
+    const int nrow_blocks = (E + RS_WAVES - 1) / RS_WAVES;
+    if ((int)blockIdx.x >= nrow_blocks) {
+        const int t = blockIdx.x - nrow_blocks;
+        const float inv = token_inv_rms(a, t, lds);
         if (th == 0) a.inv_rms[t] = inv;
-        for (int e = th; e < E; e += 256) {
-            float v = a.z[t * E + e] * inv;
-            if (a.bias) v += a.bias[e];
-            zs[e] = v;
-        }
-        __syncthreads();
-        if (wave == 0)
-            wave_topk(zs, E, a.k, a.idx + t * a.k, a.gate + t * a.k, a.u_idx ? a.u_idx + t * a.k : nullptr,
-                      a.u_gate ? a.u_gate + t * a.k : nullptr);
-        __syncthreads();
-        if (!a.route_only) prep_token(a, t, red, inv);
-        __syncthreads();
+        if (!a.route_only) prep_token(a, t, nullptr, inv);
+        return;
     }
-    __threadfence_block();
-    small_permute(a, (int32_t *)lds);
+    const int e = blockIdx.x * RS_WAVES + wave;
+    const float *wrow = a.Wr + (size_t)(e < E ? e : 0) * d;
+    float *xs = lds;  // [T][d]
+    for (int c0 = 0; c0 < d; c0 += 64 * 4 * RS_MAXJ) {
+        float4 wv[RS_MAXJ];
+#pragma unroll
+        for (int j = 0; j < RS_MAXJ; ++j) {
+            const int i = c0 + lane * 4 + 256 * j;
+            wv[j] = (e < E && i < d) ? *(const float4 *)(wrow + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (c0 == 0) {
+            for (int i = th; i < T * d; i += 256)
+                xs[i] = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
+            __syncthreads();
+        }
+        for (int t = 0; t < T; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < RS_MAXJ; ++j) {
+                const int i = c0 + lane * 4 + 256 * j;
+                if (i < d) {
+                    const float4 xv = *(const float4 *)(xs + t * d + i);
+                    acc += wv[j].x * xv.x + wv[j].y * xv.y + wv[j].z * xv.z + wv[j].w * xv.w;
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0 && e < E) {
+                if (c0 == 0) a.z[t * E + e] = acc;
+                else a.z[t * E + e] += acc;
+            }
+        }
+    }
+}
+
+// Routing only, T <= 8: one block takes the top-k and writes every output.
+__global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
+    extern __shared__ uint32_t lds_u[];
+    const SmallRoute L(lds_u, a.E);
+    small_route_compute(a, L);
+    small_route_write(a, L);
 }
 
 // -------------------------------------------------------- large-T pieces
@@ -320,14 +181,17 @@ __global__ __launch_bounds__(256) void prep_x_kernel(LayerArgs a) {
 }
 
 // Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e], fp32,
-// 64x64 output tile per block, 16x16 threads with 4x4 outputs each.
+// 64x64 output tile per block, 16x16 threads with 4x4 outputs each.  Each
+// 32-column slab is summed on its own and the slab sums are added with
+// compensated (Kahan) summation, so the error stays near one fp32 rounding
+// of the logit instead of growing with d.
 __global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
     __shared__ float xs[32][65];
     __shared__ float ws[32][65];
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
     const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
     const int d = a.d;
-    float acc[4][4] = {};
+    float acc[4][4] = {}, comp[4][4] = {};
     for (int k0 = 0; k0 < d; k0 += 32) {
         for (int i = threadIdx.x; i < 64 * 32; i += 256) {
             int r = i / 32, c = i % 32;
@@ -341,6 +205,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
             ws[c][r] = (e < a.E) ? a.Wr[(size_t)e * d + k0 + c] : 0.f;
         }
         __syncthreads();
+        float part[4][4] = {};
 #pragma unroll 8
         for (int c = 0; c < 32; ++c) {
             float xv[4], wv[4];
@@ -349,8 +214,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += xv[i] * wv[j];
+                for (int j = 0; j < 4; ++j) part[i][j] = fmaf(xv[i], wv[j], part[i][j]);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float y = part[i][j] - comp[i][j];
+                const float t = acc[i][j] + y;
+                comp[i][j] = (t - acc[i][j]) - y;
+                acc[i][j] = t;
+            }
         __syncthreads();
     }
 #pragma unroll
@@ -370,16 +244,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
 __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T) return;
-    wave_topk(a.z + (size_t)t * a.E, a.E, a.k, a.idx + (size_t)t * a.k, a.gate + (size_t)t * a.k,
-              a.u_idx ? a.u_idx + (size_t)t * a.k : nullptr, a.u_gate ? a.u_gate + (size_t)t * a.k : nullptr);
+    wave_topk(a.z + (size_t)t * a.E, a.E, a.k, 1.f, nullptr, a.idx + (size_t)t * a.k, a.gate + (size_t)t * a.k,
+              a.u_idx ? a.u_idx + (size_t)t * a.k : nullptr, a.u_gate ? a.u_gate + (size_t)t * a.k : nullptr,
+              nullptr, nullptr);
 }
 
 // Any T: one block of 1024 threads.  Counts by LDS atomics (integer, so the
 // result is order independent), exclusive scan, then a stable scatter over
 // 512-token windows: within a window each expert's picks are marked in a
 // bitmap and a pick's rank is the number of marked earlier tokens.
-constexpr int PW = 512;  // tokens per window
-__global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a) {
+// Window of PW tokens (512, or 256 when E > 512 so the bitmaps fit in LDS).
+__global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW) {
     extern __shared__ int32_t sh[];
     const int th = threadIdx.x, nth = 1024;
     const int E = a.E, k = a.k, T = a.T;
@@ -388,7 +263,7 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a) {
     int32_t *run = sh + E;              // [E] running slot per expert
     int32_t *scan = sh + 2 * E;         // [1024]
     uint32_t *bm = (uint32_t *)(sh + 2 * E + 1024);  // [E][PW/32]
-    constexpr int BW = PW / 32;
+    const int BW = PW / 32;
     for (int e = th; e < E; e += nth) hist[e] = 0;
     __syncthreads();
     for (int64_t i = th; i < n; i += nth) atomicAdd(&hist[a.idx[i]], 1);
@@ -500,16 +375,21 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a) {
 }
 
 // ------------------------------------------------------------- launchers
-hipError_t launch_route_small(const LayerArgs &a, hipStream_t s) {
-    int blocks = (a.E + RS_EPB - 1) / RS_EPB;
-    size_t lds = sizeof(float) * (size_t)small_lds_floats(a);
-    if (a.x_is_bf16) {
-        allow_lds(route_small_kernel<1>, lds);
-        hipLaunchKernelGGL(route_small_kernel<1>, dim3(blocks), dim3(256), lds, s, a);
-    } else {
-        allow_lds(route_small_kernel<0>, lds);
-        hipLaunchKernelGGL(route_small_kernel<0>, dim3(blocks), dim3(256), lds, s, a);
-    }
+hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s) {
+    const int blocks = (a.E + RS_WAVES - 1) / RS_WAVES + a.T;
+    const size_t lds = sizeof(float) * (size_t)a.T * a.d;
+    if (lds > LDS_LIMIT) return hipErrorInvalidValue;
+    if (a.x_is_bf16)
+        hipLaunchKernelGGL(route_logits_small_kernel<1>, dim3(blocks), dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL(route_logits_small_kernel<0>, dim3(blocks), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
+    const size_t lds = 4 * (size_t)small_route_lds_words(a.E);
+    if (lds > LDS_LIMIT) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_small_finish_kernel, dim3(1), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -529,9 +409,10 @@ hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route_permute(const LayerArgs &a, hipStream_t s) {
-    size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + 1024) + sizeof(uint32_t) * (size_t)a.E * (PW / 32);
-    allow_lds(route_permute_kernel, lds);
-    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), lds, s, a);
+    const int pw = a.E <= 512 ? 512 : 256;
+    const size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + 1024) + sizeof(uint32_t) * (size_t)a.E * (pw / 32);
+    if (lds > LDS_LIMIT) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), lds, s, a, pw);
     return hipGetLastError();
 }
 

@@ -1,0 +1,302 @@
+// Wave- and block-level routing helpers shared by the routing kernels and
+// the decode-size gate/up kernel: ordered top-k with gates, and the small-T
+// routing state (picks, per-expert token masks, work items, outputs).
+//
+// Top-k selection is by (logit desc, expert index asc); gates are the softmax
+// renormalised over the k picks (per-layer routing of 10 of 512 experts:
+// greenbean-ai, "Strata 如何讓 12GB 顯卡跑 Qwen3.8-Flash-Next？", section 一).
+#pragma once
+#include "common.hpp"
+
+namespace strata {
+
+// Monotone map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t f32_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// DPP lane swap within rows of 16 (quad perms and row mirrors).
+template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Maximum of a 64-bit key over the wave, returned uniform: the 16-lane rows
+// reduce through DPP lane swaps, the four row maxima through readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = u64_max(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = u64_max(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = u64_max(v, dpp64<0x141>(v));  // row_half_mirror
+    v = u64_max(v, dpp64<0x140>(v));  // row_mirror
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        m = u64_max(m, ((uint64_t)hi << 32) | lo);
+    }
+    return m;
+}
+
+// Ordered top-k of E logits z[e] * scale + bias[e] by one wave (JM = E/64
+// rounded up to 8 or 16).  Each lane sorts its JM candidates once by the
+// composite key (value, ~index); every round takes the wave maximum of the
+// lanes' heads and the lane owning it pops its head.  Lane r < k ends with
+// pick r: *e_out, *z_out.
+template <int JM>
+__device__ __forceinline__ void wave_topk_picks(const float *z, int E, int k, float scale, const float *bias,
+                                                int *e_out, float *z_out) {
+    const int lane = threadIdx.x & 63;
+    // all loads first, from clamped addresses, so they are in flight together
+    float zv[JM], bv[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) bv[j] = 0.f;
+    if (bias) {
+#pragma unroll
+        for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+    }
+    uint64_t key[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int e = lane + 64 * j;
+        const float v = zv[j] * scale + bv[j];
+        key[j] = (e < E) ? (((uint64_t)f32_key(v) << 32) | (uint32_t)(~(uint32_t)e)) : 0;
+    }
+    // bitonic sort, descending
+#pragma unroll
+    for (int kk = 2; kk <= JM; kk <<= 1)
+#pragma unroll
+        for (int jj = kk >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+            for (int i = 0; i < JM; ++i) {
+                const int l = i ^ jj;
+                if (l > i) {
+                    const bool desc = (i & kk) == 0;
+                    const uint64_t a = key[i], b = key[l];
+                    const bool sw = desc ? (a < b) : (a > b);
+                    key[i] = sw ? b : a;
+                    key[l] = sw ? a : b;
+                }
+            }
+    int my_e = 0;
+    float my_z = 0.f;
+    for (int r = 0; r < k; ++r) {
+        const uint64_t m = wave_max_u64(key[0]);
+        const uint32_t kh = (uint32_t)(m >> 32);
+        const int e = (int)(~(uint32_t)m);
+        const uint32_t u = (kh & 0x80000000u) ? (kh & 0x7FFFFFFFu) : ~kh;
+        if (lane == r) {
+            my_e = e;
+            my_z = __uint_as_float(u);
+        }
+        if (key[0] == m) {  // the owner pops its head
+#pragma unroll
+            for (int j = 0; j < JM - 1; ++j) key[j] = key[j + 1];
+            key[JM - 1] = 0;
+        }
+    }
+    *e_out = my_e;
+    *z_out = my_z;
+}
+
+// Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
+__device__ __forceinline__ void wave_topk(const float *z, int E, int k, float scale, const float *bias,
+                                          int32_t *idx_out, float *gate_out, int32_t *idx_out2, float *gate_out2,
+                                          int32_t *idx_lds, float *gate_lds) {
+    const int lane = threadIdx.x & 63;
+    int e;
+    float v;
+    if (E <= 512)
+        wave_topk_picks<8>(z, E, k, scale, bias, &e, &v);
+    else
+        wave_topk_picks<16>(z, E, k, scale, bias, &e, &v);
+    const float top = __shfl(v, 0, WAVE);
+    const float p = (lane < k) ? expf(v - top) : 0.f;
+    const float s = wave_sum(p);
+    if (lane < k) {
+        const float g = p / s;
+        if (idx_out) idx_out[lane] = e;
+        if (gate_out) gate_out[lane] = g;
+        if (idx_out2) idx_out2[lane] = e;
+        if (gate_out2) gate_out2[lane] = g;
+        if (idx_lds) idx_lds[lane] = e;
+        if (gate_lds) gate_lds[lane] = g;
+    }
+}
+
+__device__ __forceinline__ bool is_resident(const uint32_t *mask, int e) {
+    return !mask || ((mask[e >> 5] >> (e & 31)) & 1u);
+}
+
+// Exclusive scan of one int per thread over the block; *total = block sum.
+__device__ __forceinline__ int block_excl_scan(int v, int *tmp /* >= 16 ints */, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, WAVE);
+        if (lane >= o) inc += t;
+    }
+    __syncthreads();
+    if (lane == 63) tmp[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int sw = tmp[w];
+        base += (w < wave) ? sw : 0;
+        tot += sw;
+    }
+    *total = tot;
+    return base + inc - v;
+}
+
+// ----------------------------------------------------- small-T routing state
+// LDS words: per-expert token masks [E], resident-picked bitmap [32],
+// picks [256] (ids), gates [256], scratch [16].
+__host__ __device__ constexpr int small_route_lds_words(int E) { return E + 32 + 256 + 256 + 16; }
+
+struct SmallRoute {
+    int32_t *tokmask;
+    uint32_t *picked;
+    int32_t *sidx;
+    float *sgate;
+    int32_t *tmp;
+    __device__ SmallRoute(uint32_t *base, int E)
+        : tokmask((int32_t *)base),
+          picked(base + E),
+          sidx((int32_t *)(base + E + 32)),
+          sgate((float *)(base + E + 32 + 256)),
+          tmp((int32_t *)(base + E + 32 + 512)) {}
+};
+
+// Every block: top-k of its T <= 8 tokens (one wave per token) from the
+// unnormalised logits z and the tokens' inverse RMS, then per-expert token
+// masks and the bitmap of picked resident experts.
+__device__ __forceinline__ void small_route_compute(const LayerArgs &a, const SmallRoute &L) {
+    const int th = threadIdx.x, wave = th >> 6, nw = blockDim.x >> 6;
+    const int E = a.E, k = a.k, T = a.T;
+    for (int i = th; i < E; i += blockDim.x) L.tokmask[i] = 0;
+    if (th < 32) L.picked[th] = 0;
+    for (int t = wave; t < T; t += nw)
+        wave_topk(a.z + t * E, E, k, a.inv_rms[t], a.bias, nullptr, nullptr, nullptr, nullptr, L.sidx + t * k,
+                  L.sgate + t * k);
+    __syncthreads();
+    if (th < T * k) {
+        const int e = L.sidx[th];
+        atomicOr(&L.tokmask[e], 1 << (th / k));
+        if (is_resident(a.mask, e)) atomicOr(&L.picked[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+}
+
+// Work item `item` of this routing: the item-th picked resident expert in
+// ascending order, or, for item == (number of them), the shared expert with
+// all T tokens.  Slots of expert e start at the number of picks of experts
+// below e.  Returns false past the last item.  toks[j] = token of slot j.
+__device__ __forceinline__ bool small_route_item(const LayerArgs &a, const SmallRoute &L, int item, WorkItem &it,
+                                                 int *toks) {
+    const int th = threadIdx.x, n = a.T * a.k;
+    int nres = 0;
+    for (int w = 0; w < 32; ++w) nres += __popc(L.picked[w]);
+    if (item > nres) return false;
+    if (item == nres) {
+        it = WorkItem{a.E, n, a.T};
+        for (int j = 0; j < a.T; ++j) toks[j] = j;
+        return true;
+    }
+    if (th < n) {
+        const int e = L.sidx[th], t = th / a.k;
+        const uint32_t mk = (uint32_t)L.tokmask[e];
+        if (is_resident(a.mask, e) && (int)__ffs(mk) - 1 == t) {  // first pick of e
+            int rank = 0;
+            for (int w = 0; w < (e >> 5); ++w) rank += __popc(L.picked[w]);
+            rank += __popc(L.picked[e >> 5] & ((1u << (e & 31)) - 1u));
+            if (rank == item) {
+                int below = 0;
+                for (int j = 0; j < n; ++j) below += L.sidx[j] < e ? 1 : 0;
+                L.tmp[8] = e;
+                L.tmp[9] = below;
+            }
+        }
+    }
+    __syncthreads();
+    const int e = L.tmp[8];
+    const uint32_t mk = (uint32_t)L.tokmask[e];
+    it = WorkItem{e, L.tmp[9], (int32_t)__popc(mk)};
+    int j = 0;
+    for (int t = 0; t < a.T; ++t)
+        if ((mk >> t) & 1u) toks[j++] = t;
+    return true;
+}
+
+// One block: write the routing outputs (ids, gates, counts, offsets,
+// permutation, work list for the down kernel, miss list, user copies).
+__device__ __forceinline__ void small_route_write(const LayerArgs &a, const SmallRoute &L) {
+    const int th = threadIdx.x, nth = blockDim.x;
+    const int E = a.E, k = a.k, T = a.T, n = T * k;
+    if (th < n) {
+        a.idx[th] = L.sidx[th];
+        a.gate[th] = L.sgate[th];
+        if (a.u_idx) a.u_idx[th] = L.sidx[th];
+        if (a.u_gate) a.u_gate[th] = L.sgate[th];
+    }
+    const int ept = (E + nth - 1) / nth;
+    int c_loc = 0, a_loc = 0;
+    for (int j = 0; j < ept; ++j) {
+        const int e = th * ept + j;
+        if (e < E) {
+            const int c = __popc((uint32_t)L.tokmask[e]);
+            c_loc += c;
+            a_loc += (c > 0 && is_resident(a.mask, e)) ? 1 : 0;
+        }
+    }
+    int tot;
+    const int ex = block_excl_scan((a_loc << 16) | c_loc, L.tmp, &tot);
+    int off = ex & 0xFFFF, ai = ex >> 16;
+    for (int j = 0; j < ept; ++j) {
+        const int e = th * ept + j;
+        if (e < E) {
+            const int c = __popc((uint32_t)L.tokmask[e]);
+            a.counts[e] = c;
+            a.offsets[e] = off;
+            if (a.u_counts) a.u_counts[e] = c;
+            if (a.u_offsets) a.u_offsets[e] = off;
+            if (c > 0 && is_resident(a.mask, e)) a.items[ai++] = WorkItem{e, off, (int32_t)c};
+            off += c;
+        }
+    }
+    if (th == 0) {
+        a.offsets[E] = tot & 0xFFFF;
+        if (a.u_offsets) a.u_offsets[E] = tot & 0xFFFF;
+        a.items[tot >> 16] = WorkItem{E, n, T};
+        *a.n_items = (tot >> 16) + 1;
+    }
+    // slot of pick (t, r): offset of its expert + earlier tokens of that expert
+    if (th < n) {
+        const int e = L.sidx[th], t = th / k;
+        int below = 0;
+        for (int j = 0; j < n; ++j) below += L.sidx[j] < e ? 1 : 0;
+        const int slot = below + __popc((uint32_t)L.tokmask[e] & ((1u << t) - 1u));
+        a.perm[slot] = th;
+        a.pos[th] = slot;
+        if (a.u_perm) a.u_perm[slot] = th;
+        if (a.u_pos) a.u_pos[th] = slot;
+    }
+    const int miss = (th < n && !is_resident(a.mask, L.sidx[th])) ? 1 : 0;
+    int mt;
+    const int mp = block_excl_scan(miss, L.tmp, &mt);
+    if (miss && a.miss_te && mp < a.miss_cap) {
+        a.miss_te[2 * mp] = th / k;
+        a.miss_te[2 * mp + 1] = L.sidx[th];
+        a.miss_w[mp] = L.sgate[th];
+    }
+    if (th == 0 && a.miss_count) *a.miss_count = mt;
+}
+
+}  // namespace strata

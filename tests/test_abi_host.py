@@ -33,8 +33,8 @@ def test_workspace_sizes():
     sh = brx.shape(512, 10, 2048, 768, 3)
     assert brx.workspace_bytes(sh, 1) > 0
     assert brx.workspace_bytes(sh, 4096) > brx.workspace_bytes(sh, 5)
-    # expert outputs dominate: (T*k + T) slots x (d + 2f) fp32
-    assert brx.workspace_bytes(sh, 4096) >= 4096 * 11 * (2048 + 2 * 768) * 4
+    # per slot ((T*k + T) of them): fp32 expert output row (d) + 16-bit digit planes of h (f)
+    assert brx.workspace_bytes(sh, 4096) >= 4096 * 11 * (2048 * 4 + 768 * 2)
 
 
 @pytest.mark.parametrize("bad", [
@@ -116,5 +116,5 @@ def test_status_strings():
 
 def test_kernel_names_by_path():
     sh = brx.shape(512, 10, 2048, 768, 3)
-    assert brx.kernel_names(sh, 1)[0] == "route_small"
+    assert brx.kernel_names(sh, 1)[0] == "route_logits"
     assert "route_permute" in brx.kernel_names(sh, 4096)

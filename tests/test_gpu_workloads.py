@@ -1,0 +1,193 @@
+"""Parity at the full workload sizes: the 48-layer 5-token verify stack, the
+4096-token 2-bit prefill chunk and the Zipf-skewed masked prefill, plus
+ragged token counts on the larger-batch path.
+
+Routing (ids, gates, counts, offsets, permutation, miss list) is compared
+for every token; layer outputs for every token where the oracle is cheap
+(the verify stack, ragged cases) and on a seeded sample of tokens otherwise
+(the oracle evaluates those tokens' experts one by one).
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+from tests import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _upload_layer(w, layer, host_codes, attempt=0, bias=None, mask=None):
+    """Generate one layer's codes into host_codes and upload everything."""
+    t = _torch()
+    synth.layer_codes_into(w, layer, host_codes.ctypes.data)
+    scales = synth.layer_scales(w, layer)
+    Wr = synth.router_weights(w, layer, attempt)
+    import bit_routed_expert_amd as brx
+    ld = brx.LayerData(router_w=G.dev(Wr), codes=t.from_numpy(host_codes).cuda(), scales=G.dev(scales),
+                       router_bias=None if bias is None else G.dev(bias),
+                       resident_mask=None if mask is None else G.dev(mask))
+    return ld, scales, Wr
+
+
+def test_verify_stack_48_layers_five_tokens():
+    """48 independent full-size 3-bit layers, T = 5, fp32 residual with RMS
+    normalisation between layers.  Each layer's router is redrawn (attempt
+    counter) until the 5 tokens' logits have top-(k+1) margins >= 1e-3 on the
+    oracle's own layer input."""
+    w = synth.WORKLOADS["mtp_verify"]
+    T, L = w.tokens, w.layers
+    t0 = time.time()
+    host = np.empty(w.experts_total * w.code_bytes_per_expert, dtype=np.uint8)
+    x0 = None
+    layers, ref_route, attempts = [], [], []
+    # first layer input: bf16 tokens drawn with margins against layer 0's router
+    Wr0 = synth.router_weights(w, 0, 0)
+    x0, _ = W.draw_tokens(w, Wr0, None, range(T))
+    xl = synth.bf16_to_f32(x0)
+    for l in range(L):
+        u = oracle.layer_input(xl, l)
+        attempt = 0
+        while True:
+            Wr = synth.router_weights(w, l, attempt)
+            if oracle.topk_margin(oracle.logits(u, Wr), w.top_k).min() >= W.MARGIN:
+                break
+            attempt += 1
+        ld, scales, Wr = _upload_layer(w, l, host, attempt)
+        layers.append(ld)
+        attempts.append(attempt)
+        r = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, Wr, host, scales, grouped=False)
+        ref_route.append(r)
+        y_last = r["out"]
+        xl = oracle.residual_add(xl, r["out"])
+    print(f"verify stack: oracle + upload {time.time() - t0:.1f}s", flush=True)
+    got = G.run_forward(w, layers, G.dev(x0), 0, T)
+    ry = G.assert_close(got["y"], y_last, what="y_47")
+    rx = G.assert_close(got["resid"], xl, what="x_48")
+    print(f"y_47 max-abs/RMS {ry:.2e}, x_48 {rx:.2e}")
+    # the 48-layer call equals 48 chained one-layer calls, bit for bit; the
+    # chain also exposes the GPU's own input to every layer
+    t = _torch()
+    xc, xd = G.dev(x0), 0
+    gpu_inputs = [synth.bf16_to_f32(x0)]
+    for l in range(L):
+        one = G.run_forward(w, [layers[l]], xc, xd, T, flags=(1 if l > 0 else 0))
+        np.testing.assert_array_equal(one["route"][0]["topk_idx"], got["route"][l]["topk_idx"])
+        np.testing.assert_array_equal(one["route"][0]["topk_w"], got["route"][l]["topk_w"])
+        xc, xd = t.from_numpy(one["resid"]).cuda(), 1
+        gpu_inputs.append(one["resid"])
+    np.testing.assert_array_equal(one["y"], got["y"])
+    np.testing.assert_array_equal(one["resid"], got["resid"])
+    # routing per layer: ids (and counts, permutation) bit-exact against the
+    # oracle's own chain (the margins make them unique); gates within 1e-6 of
+    # the oracle evaluated on the same layer input the GPU saw (from layer 1
+    # on the two residual streams differ by the tolerated output error, which
+    # moves gates by ~1e-5 but never the ordered ids)
+    for l in range(L):
+        gr = got["route"][l]
+        ref = ref_route[l]
+        np.testing.assert_array_equal(gr["topk_idx"], ref["idx"])
+        for key in ("counts", "offsets", "perm", "pos"):
+            np.testing.assert_array_equal(gr[key], ref[key])
+        u_gpu = oracle.layer_input(gpu_inputs[l], l)
+        idx_g, gate_g = oracle.select(oracle.logits(u_gpu, synth.router_weights(w, l, attempts[l])), w.top_k)
+        np.testing.assert_array_equal(idx_g, ref["idx"])
+        assert np.max(np.abs(gr["topk_w"] - gate_g)) <= G.GATE_TOL, f"layer {l} gates"
+
+
+def _prefill_case(name, call=0, sample=48):
+    w = synth.WORKLOADS[name]
+    T = w.tokens_per_call
+    t0 = time.time()
+    L = W.layer_data(w, 0)
+    tok = range(call * T, (call + 1) * T)
+    x, _ = W.draw_tokens(w, L["Wr"], L["bias"], tok)
+    u = synth.bf16_to_f32(x)
+    z = oracle.logits(u, L["Wr"], L["bias"])
+    idx, gate = oracle.select(z, w.top_k)
+    counts, offsets, perm, pos = oracle.permute(idx, w.n_experts)
+    te, mw, nm = oracle.misses(idx, gate, L["mask"], T * w.top_k)
+    rows = np.sort(np.random.default_rng(1234 + call).choice(T, sample, replace=False))
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u[rows], L["Wr"], L["codes"],
+                           L["scales"], bias=L["bias"], mask=L["mask"], grouped=False)
+    print(f"{name} call {call}: oracle {time.time() - t0:.1f}s", flush=True)
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    gr = got["route"][0]
+    G.assert_route_equal(gr, dict(idx=idx, gate=gate, counts=counts, offsets=offsets, perm=perm, pos=pos))
+    r = G.assert_close(got["y"][rows], ref["out"], what=f"{name} sampled rows")
+    np.testing.assert_array_equal(got["resid"][rows], (u[rows] + got["y"][rows]).astype(np.float32))
+    if L["mask"] is not None:
+        assert int(got["miss_count"][0]) == nm
+        np.testing.assert_array_equal(got["miss_te"][0][:nm], te)
+        assert np.max(np.abs(got["miss_w"][0][:nm] - mw)) <= G.GATE_TOL
+        hit = 1 - nm / (T * w.top_k)
+        print(f"hit rate {hit:.3f}, max expert load {counts.max()}, mean {counts.mean():.1f}")
+    print(f"{name} sampled max-abs/RMS {r:.2e}")
+
+
+def test_prefill_chunk_2bit_4096():
+    _prefill_case("prefill_2bit")
+
+
+@pytest.mark.parametrize("call", [0, 7])
+def test_zipf_prefill_masked_chunks(call):
+    _prefill_case("zipf_prefill", call=call)
+
+
+@pytest.mark.parametrize("T", [9, 37, 130])
+def test_ragged_batches_full_size_layer(T):
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 1)
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=7)
+    u = synth.bf16_to_f32(x)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, L["Wr"], L["codes"], L["scales"],
+                           grouped=False)
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 20])
+def test_small_layer_token_counts(T):
+    w = synth.WORKLOADS["tiny"]
+    L = W.layer_data(w, 0)
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=11)
+    u = synth.bf16_to_f32(x)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, L["Wr"], L["codes"], L["scales"])
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+
+
+def test_route_only_entry_point():
+    import bit_routed_expert_amd as brx
+    t = _torch()
+    for name, T in (("decode", 3), ("decode", 300)):
+        w = synth.WORKLOADS[name]
+        L = W.layer_data(w, 2)
+        x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=13)
+        idx, gate = oracle.select(oracle.logits(synth.bf16_to_f32(x), L["Wr"]), w.top_k)
+        counts, offsets, perm, pos = oracle.permute(idx, w.n_experts)
+        sh = G.shape_of(w)
+        nb = brx.workspace_bytes(sh, T)
+        ws = t.zeros(nb, dtype=t.uint8, device="cuda")
+        out = dict(topk_idx=t.empty((T, w.top_k), dtype=t.int32, device="cuda"),
+                   topk_w=t.empty((T, w.top_k), dtype=t.float32, device="cuda"),
+                   counts=t.empty(w.n_experts, dtype=t.int32, device="cuda"),
+                   offsets=t.empty(w.n_experts + 1, dtype=t.int32, device="cuda"),
+                   perm=t.empty(T * w.top_k, dtype=t.int32, device="cuda"),
+                   pos=t.empty(T * w.top_k, dtype=t.int32, device="cuda"))
+        brx.route(sh, brx.LayerData(router_w=G.dev(L["Wr"]), codes=None, scales=None), G.dev(x), 0, T, out, ws, nb)
+        t.cuda.synchronize()
+        G.assert_route_equal({kk: v.cpu().numpy() for kk, v in out.items()},
+                             dict(idx=idx, gate=gate, counts=counts, offsets=offsets, perm=perm, pos=pos))
