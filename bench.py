@@ -120,11 +120,13 @@ def main():
                 hip.destroy(e)
     kern_avg = {n: (float(np.mean(v)) if v else None) for n, v in kern_us.items()}
 
-    # dominant kernel: expert gate/up GEMV.  Algorithmic bytes per launch: the
-    # gate and up codes + fp16 scales of the 11 experts one token needs.
+    # dominant kernel: the gate/up expert kernel (it also takes the top-k from
+    # the logits).  Algorithmic bytes per launch: the gate and up codes + fp16
+    # scales of the 11 experts one token needs (logits and activations are
+    # a few KB and are left out).
     per_expert_gu = 2 * (d * f * w.bits // 8 + (d * f // 256) * 2)
     n_exp = k + 1
-    dom = "gemv_gateup"
+    dom = "route_gemv_gateup"
     dom_bytes = n_exp * per_expert_gu
     dom_us = kern_avg.get(dom)
     roof = None

@@ -1,0 +1,8 @@
+// Down expert kernels for 2-bit codes (one translation unit per
+// kernel family and code width, so the instantiations compile in parallel).
+#include "gemv_impl.hpp"
+
+namespace strata {
+template hipError_t down_launch<2>(const LayerArgs &, int, hipStream_t);
+template hipError_t down_rows_launch<2>(const LayerArgs &, hipStream_t);
+}  // namespace strata

@@ -1,0 +1,8 @@
+// Gate/up expert kernels for 3-bit codes (one translation unit per
+// kernel family and code width, so the instantiations compile in parallel).
+#include "gemv_impl.hpp"
+
+namespace strata {
+template hipError_t gateup_launch<3>(const LayerArgs &, int, hipStream_t);
+template hipError_t gateup_small_launch<3>(const LayerArgs &, int, hipStream_t);
+}  // namespace strata
