@@ -20,19 +20,28 @@ constexpr int SMALL_T = 8;
 
 struct Layout {
     size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hq, hsum,
-        hscl, Y, out, xres0, xres1, miss_count, total;
+        hscl, xa, sx, ha, hs, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
+bool small_path(const strata_moe_shape &s, int64_t T) {
+    return T <= SMALL_T && (size_t)T * s.d_model * sizeof(float) <= 64 * 1024;
+}
+
+// Work items: one per picked expert (decode path), else tiles of up to
+// GEMM_BM tokens per resident expert with picks plus the shared expert's.
 int64_t max_items_for(const strata_moe_shape &s, int64_t T) {
-    if (T <= SMALL_T) return std::min<int64_t>(s.n_experts, T * s.top_k) + 1;
-    return (T * s.top_k + CHUNK_TOK - 1) / CHUNK_TOK + s.n_experts + (T + CHUNK_TOK - 1) / CHUNK_TOK + 2;
+    if (small_path(s, T)) return std::min<int64_t>(s.n_experts, T * s.top_k) + 1;
+    return (T * s.top_k + GEMM_BM - 1) / GEMM_BM + s.n_experts + (T + GEMM_BM - 1) / GEMM_BM + 2;
 }
 
 Layout layout(const strata_moe_shape &s, int64_t T) {
     Layout l{};
     const int64_t E = s.n_experts, k = s.top_k, d = s.d_model, f = s.d_ff;
     const int64_t slots = T * k + T;
+    const bool sp = small_path(s, T);
+    const int64_t Tq = sp ? T : 0, Sq = sp ? slots : 0;   // digit planes: decode path only
+    const int64_t Tg = sp ? 0 : T, Sg = sp ? 0 : slots;   // bf16 operands: GEMM path only
     l.max_items = max_items_for(s, T);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
@@ -47,12 +56,16 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.inv_rms = take(4 * T);
     l.items = take(sizeof(WorkItem) * l.max_items);
     l.n_items = take(4);
-    l.xq = take((size_t)T * (d / 32) * XPLANES * 16);
-    l.xsum = take(4 * T * (d / 32));
-    l.xscl = take(4 * T * ((d + 255) / 256));
-    l.hq = take((size_t)slots * (f / 32) * XPLANES * 16);
-    l.hsum = take(4 * slots * (f / 32));
-    l.hscl = take(4 * slots * (f / 32));
+    l.xq = take((size_t)Tq * (d / 32) * XPLANES * 16);
+    l.xsum = take(4 * Tq * (d / 32));
+    l.xscl = take(4 * Tq * ((d + 255) / 256));
+    l.hq = take((size_t)Sq * (f / 32) * XPLANES * 16);
+    l.hsum = take(4 * Sq * (f / 32));
+    l.hscl = take(4 * Sq * (f / 32));
+    l.xa = take((size_t)2 * Tg * d * 2);
+    l.sx = take(4 * Tg * (d / 128));
+    l.ha = take((size_t)2 * Sg * f * 2);
+    l.hs = take(4 * Sg * (f / 32));
     l.Y = take(sizeof(float) * slots * d);
     l.out = take(sizeof(float) * T * d);
     l.xres0 = take(sizeof(float) * T * d);
@@ -69,11 +82,8 @@ strata_status check_shape(const strata_moe_shape *s) {
     if (s->d_model <= 0 || s->d_ff <= 0 || s->d_model % 128 || s->d_ff % 128) return STRATA_EINVAL;
     if (s->bits != 3 && s->bits != 2) return STRATA_EUNSUPPORTED;
     if (!gemv_supported(s->d_model, s->d_ff, s->bits)) return STRATA_EUNSUPPORTED;
+    if (!gemm_supported(s->d_model, s->d_ff)) return STRATA_EUNSUPPORTED;
     return STRATA_OK;
-}
-
-bool small_path(const strata_moe_shape &s, int T) {
-    return T <= SMALL_T && (size_t)T * s.d_model * sizeof(float) <= 64 * 1024;
 }
 
 void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char *ws, int T) {
@@ -102,6 +112,10 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.hsum = (int32_t *)(ws + l.hsum);
     a.hscl = (float *)(ws + l.hscl);
     a.Y = (float *)(ws + l.Y);
+    a.xa = (uint16_t *)(ws + l.xa);
+    a.sx = (float *)(ws + l.sx);
+    a.ha = (uint16_t *)(ws + l.ha);
+    a.hs = (float *)(ws + l.hs);
 }
 
 void set_route_out(LayerArgs &a, const strata_route_out *r) {
@@ -146,10 +160,10 @@ strata_status route_layer(LayerArgs &a, const strata_moe_shape &s, int T, Record
         RUN(launch_route_logits_small(a, rec.s));
         if (a.route_only) RUN(launch_route_small_finish(a, rec.s));
     } else {
-        RUN(launch_prep_x(a, rec.s));
+        RUN(launch_gemm_prep(a, rec.s));
         RUN(launch_route_logits(a, rec.s));
         RUN(launch_route_topk(a, rec.s));
-        RUN(launch_route_permute(a, rec.s));
+        RUN(launch_route_permute(a, GEMM_BM, rec.s));
     }
     return STRATA_OK;
 }
@@ -178,8 +192,8 @@ const char *strata_status_str(strata_status s) {
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max) {
     static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
     static const char *small4[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
-    static const char *large[] = {"prep_x", "route_logits", "route_topk", "route_permute",
-                                  "gemv_gateup", "gemv_down", "combine"};
+    static const char *large[] = {"gemm_prep", "route_logits", "route_topk", "route_permute",
+                                  "gemm_gateup", "gemm_down", "combine"};
     if (check_shape(shape) != STRATA_OK) return 0;
     const bool sp = small_path(*shape, T);
     const bool rows = sp && down_rows_fits(T, shape->top_k, shape->d_ff);
@@ -253,6 +267,7 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
             a.x_is_bf16 = 0;
         }
         a.normalize = (l > 0) || (flags & STRATA_NORM_FIRST);
+        a.xpasses = (a.x_is_bf16 && !a.normalize) ? 1 : 2;
         a.route_only = 0;
         if (route_out) set_route_out(a, &route_out[l]);
         if (miss_te) {
@@ -274,8 +289,8 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
                 RUN(launch_combine(a, rec.s));
             }
         } else {
-            RUN(launch_gemv_gateup(a, (int)lay.max_items, rec.s));
-            RUN(launch_gemv_down(a, (int)lay.max_items, rec.s));
+            RUN(launch_gemm_gateup(a, (int)lay.max_items, rec.s));
+            RUN(launch_gemm_down(a, (int)lay.max_items, rec.s));
             RUN(launch_combine(a, rec.s));
         }
     }

@@ -9,6 +9,8 @@ namespace strata {
 constexpr int WAVE = 64;
 constexpr int CHUNK_TOK = 8;      // tokens one expert work item carries (GEMV path)
 constexpr int XPLANES = 6;        // base-16 digit planes of an activation (24-bit fixed point)
+constexpr int GEMM_BM = 96;       // tokens per expert tile (GEMM path)
+constexpr int GEMM_MAX_K = 4096;  // largest d and f the GEMM path stages
 constexpr float RMS_EPS = 1e-6f;
 
 // Largest |X| that P balanced base-16 digits in [-8, 7] represent symmetrically:
@@ -55,6 +57,33 @@ template <int P> __device__ __forceinline__ void to_digits(int X, int d[P]) {
         d[p] = v;
         X = (X - v) >> 4;
     }
+}
+
+// 1 / sqrt(mean(x_t^2) + eps) of token t (1 when the layer does not
+// normalise); whole block, red = LDS scratch of blockDim/64 floats.
+template <typename Args>
+__device__ float token_inv_rms(const Args &a, int t, float *red) {
+    if (!a.normalize) return 1.f;
+    const int d = a.d, nth = blockDim.x, th = threadIdx.x;
+    float ss = 0.f;
+    for (int i0 = 0; i0 < d; i0 += 8 * nth) {  // 8 independent loads in flight per pass
+        float xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const size_t o = (size_t)t * d + min(i0 + th + j * nth, d - 1);
+            xv[j] = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += (i0 + th + j * nth < d) ? xv[j] * xv[j] : 0.f;
+    }
+    ss = wave_sum(ss);
+    __syncthreads();
+    if ((th & 63) == 0) red[th >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < nth / 64; ++w) tot += red[w];
+    __syncthreads();
+    return 1.f / sqrtf(tot / (float)d + RMS_EPS);
 }
 
 // Work item of the expert kernels: up to CHUNK_TOK tokens of one expert.
@@ -110,6 +139,13 @@ struct LayerArgs {
     int32_t *hsum;
     float *hscl;
     float *Y;            // [slots][d] expert outputs (larger T)
+    // GEMM path: bf16 hi/lo activations, columns permuted inside each
+    // 128-column step, and their sums over each step (x) or 32-feature group (h)
+    uint16_t *xa;        // [2][T][d]
+    float *sx;           // [T][d/128]
+    uint16_t *ha;        // [2][slots][f]
+    float *hs;           // [slots][f/32]
+    int xpasses;         // 1 when the lo half of xa is zero (bf16 input, no normalisation)
     // combine outputs
     float *out;          // [T][d] layer output
     float *x_next;       // [T][d] residual stream after this layer (nullable)
@@ -120,15 +156,17 @@ struct LayerArgs {
 hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s);
-hipError_t launch_prep_x(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
-hipError_t launch_route_permute(const LayerArgs &a, hipStream_t s);
-hipError_t launch_gemv_gateup(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s);
 hipError_t launch_gemv_down(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemv_down_rows(const LayerArgs &a, hipStream_t s);
 bool down_rows_fits(int T, int k, int f);
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gemm_prep(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gemm_gateup(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_gemm_down(const LayerArgs &a, int max_items, hipStream_t s);
+bool gemm_supported(int d, int f);
 bool gemv_supported(int d, int f, int bits);
 
 }  // namespace strata

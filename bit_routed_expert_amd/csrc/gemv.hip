@@ -4,8 +4,6 @@
 
 namespace strata {
 
-extern template hipError_t gateup_launch<3>(const LayerArgs &, int, hipStream_t);
-extern template hipError_t gateup_launch<2>(const LayerArgs &, int, hipStream_t);
 extern template hipError_t gateup_small_launch<3>(const LayerArgs &, int, hipStream_t);
 extern template hipError_t gateup_small_launch<2>(const LayerArgs &, int, hipStream_t);
 extern template hipError_t down_launch<3>(const LayerArgs &, int, hipStream_t);
@@ -18,10 +16,6 @@ bool gemv_supported(int d, int f, int bits) { return gemv_supported_impl(d, f, b
 bool down_rows_fits(int T, int k, int f) {
     const int R = 64 / pick_slices(f);
     return T <= CHUNK_TOK && down_rows_lds(T, k, f, R, nt_round(ntmax_for(T))) <= LDS_LIMIT;
-}
-
-hipError_t launch_gemv_gateup(const LayerArgs &a, int max_items, hipStream_t s) {
-    return a.bits == 3 ? gateup_launch<3>(a, max_items, s) : gateup_launch<2>(a, max_items, s);
 }
 
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s) {

@@ -3,6 +3,5 @@
 #include "gemv_impl.hpp"
 
 namespace strata {
-template hipError_t gateup_launch<2>(const LayerArgs &, int, hipStream_t);
 template hipError_t gateup_small_launch<2>(const LayerArgs &, int, hipStream_t);
 }  // namespace strata

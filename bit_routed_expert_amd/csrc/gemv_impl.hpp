@@ -313,21 +313,6 @@ __host__ __device__ inline int gateup_lds_words(int d, int R, int nt) {
         default: break;                                               \
     }
 
-// Any T: work items from the routing kernels (items, n_items, perm).
-template <int BITS, int NTMAX>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(LayerArgs a, int R) {
-    extern __shared__ uint32_t lds[];
-    const int wg_per_item = a.f / (2 * R);
-    const int item = blockIdx.x / wg_per_item;
-    if (item >= *a.n_items) return;
-    const WorkItem it = a.items[item];
-    int toks[CHUNK_TOK];
-    for (int j = 0; j < it.ntok; ++j) toks[j] = slot_token(a, it, j);
-    const int j0 = (blockIdx.x % wg_per_item) * 2 * R;
-#define GU(n) gateup_body<BITS, n>(a, it, toks, R, j0, lds)
-    NT_SWITCH(GU)
-#undef GU
-}
 
 // T <= 8: every block takes the top-k of the T tokens itself from the
 // router logits (a few KB), derives its own work item and runs it; the last
@@ -562,15 +547,6 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
             default: hipLaunchKernelGGL((KER<BITS, 8>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
         }                                                                                            \
     } while (0)
-
-template <int BITS> hipError_t gateup_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / pick_slices(a.d);
-    const int nt = nt_round(ntmax_for(a.T));
-    const size_t lds = 4 * (size_t)gateup_lds_words(a.d, R, nt);
-    const dim3 grid(max_items * (a.f / (2 * R)));
-    LAUNCH_NT(gemv_gateup_kernel, BITS, nt, grid, 256, lds, s, a, R);
-    return hipGetLastError();
-}
 
 template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int R = 64 / pick_slices(a.d);

@@ -80,29 +80,6 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
 }
 
 // Inverse RMS of token t's row (1 when the layer input is not normalised).
-__device__ float token_inv_rms(const LayerArgs &a, int t, float *red) {
-    if (!a.normalize) return 1.f;
-    const int d = a.d, nth = blockDim.x, th = threadIdx.x;
-    float ss = 0.f;
-    for (int i0 = 0; i0 < d; i0 += 8 * nth) {  // 8 independent loads in flight per pass
-        float xv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const size_t o = (size_t)t * d + min(i0 + th + j * nth, d - 1);
-            xv[j] = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += (i0 + th + j * nth < d) ? xv[j] * xv[j] : 0.f;
-    }
-    ss = wave_sum(ss);
-    __syncthreads();
-    if ((th & 63) == 0) red[th >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < nth / 64; ++w) tot += red[w];
-    __syncthreads();
-    return 1.f / sqrtf(tot / (float)d + RMS_EPS);
-}
 
 
 // ------------------------------------------------------ decode-size route
@@ -168,16 +145,6 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
     const SmallRoute L(lds_u, a.E);
     small_route_compute(a, L);
     small_route_write(a, L);
-}
-
-// -------------------------------------------------------- large-T pieces
-// One block of 256 threads per token: inverse RMS and input digit planes.
-__global__ __launch_bounds__(256) void prep_x_kernel(LayerArgs a) {
-    __shared__ float red[8];
-    const int t = blockIdx.x;
-    float inv = token_inv_rms(a, t, red);
-    if (threadIdx.x == 0) a.inv_rms[t] = inv;
-    if (!a.route_only) prep_token(a, t, red, inv);
 }
 
 // Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e], fp32,
@@ -254,7 +221,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
 // 512-token windows: within a window each expert's picks are marked in a
 // bitmap and a pick's rank is the number of marked earlier tokens.
 // Window of PW tokens (512, or 256 when E > 512 so the bitmaps fit in LDS).
-__global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW) {
+__global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW, int tile) {
     extern __shared__ int32_t sh[];
     const int th = threadIdx.x, nth = 1024;
     const int E = a.E, k = a.k, T = a.T;
@@ -346,8 +313,8 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW
         __syncthreads();
     }
     if (th == 0 && a.miss_count) *a.miss_count = total;
-    // work list: ceil(count/CHUNK_TOK) items per resident expert with picks, then the shared expert
-    int ni = (th < E && is_resident(a.mask, th)) ? (hist[th] + CHUNK_TOK - 1) / CHUNK_TOK : 0;
+    // work list: ceil(count/tile) items per resident expert with picks, then the shared expert
+    int ni = (th < E && is_resident(a.mask, th)) ? (hist[th] + tile - 1) / tile : 0;
     scan[th] = ni;
     __syncthreads();
     for (int o = 1; o < nth; o <<= 1) {
@@ -362,14 +329,14 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW
         (void)off;
         int s0 = run[th] - hist[th];  // run[] now holds offsets + counts
         for (int j = 0; j < ni; ++j)
-            a.items[base + j] = WorkItem{th, s0 + j * CHUNK_TOK, min(CHUNK_TOK, hist[th] - j * CHUNK_TOK)};
+            a.items[base + j] = WorkItem{th, s0 + j * tile, min(tile, hist[th] - j * tile)};
     }
     int nr = scan[nth - 1];
     __syncthreads();
     if (th == 0) {
         int c = nr;
-        for (int t0 = 0; t0 < T; t0 += CHUNK_TOK)
-            a.items[c++] = WorkItem{E, (int32_t)(n + t0), min(CHUNK_TOK, T - t0)};
+        for (int t0 = 0; t0 < T; t0 += tile)
+            a.items[c++] = WorkItem{E, (int32_t)(n + t0), min(tile, T - t0)};
         *a.n_items = c;
     }
 }
@@ -393,11 +360,6 @@ hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_prep_x(const LayerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(prep_x_kernel, dim3(a.T), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(route_logits_kernel, dim3((a.E + 63) / 64, (a.T + 63) / 64), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -408,11 +370,11 @@ hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_route_permute(const LayerArgs &a, hipStream_t s) {
+hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s) {
     const int pw = a.E <= 512 ? 512 : 256;
     const size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + 1024) + sizeof(uint32_t) * (size_t)a.E * (pw / 32);
     if (lds > LDS_LIMIT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), lds, s, a, pw);
+    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), lds, s, a, pw, tile);
     return hipGetLastError();
 }
 
