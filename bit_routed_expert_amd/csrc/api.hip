@@ -20,7 +20,7 @@ constexpr int SMALL_T = 8;
 
 struct Layout {
     size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hq, hsum,
-        hscl, xa, sx, ha, hs, Y, out, xres0, xres1, miss_count, total;
+        hscl, xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -66,6 +66,9 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.sx = take(4 * Tg * (d / 128));
     l.ha = take((size_t)2 * Sg * f * 2);
     l.hs = take(4 * Sg * (f / 32));
+    const int64_t nb = sp ? 0 : route_perm_blocks((int)T);
+    l.bcnt = take(4 * nb * E);
+    l.bmiss = take(4 * nb);
     l.Y = take(sizeof(float) * slots * d);
     l.out = take(sizeof(float) * T * d);
     l.xres0 = take(sizeof(float) * T * d);
@@ -116,6 +119,8 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.sx = (float *)(ws + l.sx);
     a.ha = (uint16_t *)(ws + l.ha);
     a.hs = (float *)(ws + l.hs);
+    a.bcnt = (int32_t *)(ws + l.bcnt);
+    a.bmiss = (int32_t *)(ws + l.bmiss);
 }
 
 void set_route_out(LayerArgs &a, const strata_route_out *r) {
@@ -193,7 +198,7 @@ int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const 
     static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
     static const char *small4[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
     static const char *large[] = {"gemm_prep", "route_logits", "route_topk", "route_permute",
-                                  "gemm_gateup", "gemm_down", "combine"};
+                                  "gemm_gateup", "gemm_down", "combine"};   // route_permute: three kernels
     if (check_shape(shape) != STRATA_OK) return 0;
     const bool sp = small_path(*shape, T);
     const bool rows = sp && down_rows_fits(T, shape->top_k, shape->d_ff);

@@ -12,46 +12,66 @@
 
 namespace strata {
 
-constexpr int KMAX = 32;
+constexpr int KB = 16;          // picks gathered per batch (top_k <= 32: at most two batches)
+constexpr int CB_COLS = 1024;   // columns per block (4 per thread)
 
+// One block per (token, 1024-column segment): the token's routing is
+// block-uniform, every thread gathers 4 columns of the picked rows.
 template <int XBF16>
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int d = a.d, k = a.k, T = a.T;
-    if (gid >= (int64_t)T * d) return;
-    const int t = (int)(gid / d), i = (int)(gid % d);
+    const int segs = (d + CB_COLS - 1) / CB_COLS;
+    const int t = blockIdx.x / segs;
+    const int i = (blockIdx.x - t * segs) * CB_COLS + threadIdx.x * 4;
+    if (i >= d) return;
     const float *__restrict__ Y = a.Y;
-    // all routing reads first (independent loads), then all expert rows
-    int pr[KMAX];
-    float gr[KMAX];
-    bool on[KMAX];
+    const int64_t row = (int64_t)t * d + i;
+    float4 s = *(const float4 *)(Y + ((int64_t)T * k + t) * d + i);
+    for (int r0 = 0; r0 < k; r0 += KB) {
+        int pr[KB];
+        float gr[KB];
 #pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-        if (r < k) {
-            const int e = a.idx[t * k + r];
-            pr[r] = a.pos[t * k + r];
-            gr[r] = a.gate[t * k + r];
-            on[r] = !a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u);
+        for (int r = 0; r < KB; ++r) {
+            pr[r] = -1;
+            gr[r] = 0.f;
+            if (r0 + r < k) {
+                const int e = a.idx[t * k + r0 + r];
+                if (!a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u)) {
+                    pr[r] = a.pos[t * k + r0 + r];
+                    gr[r] = a.gate[t * k + r0 + r];
+                }
+            }
+        }
+        float4 yv[KB];
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+            yv[r] = pr[r] >= 0 ? *(const float4 *)(Y + (int64_t)pr[r] * d + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < KB; ++r) {
+            if (pr[r] >= 0) {
+                s.x = fmaf(gr[r], yv[r].x, s.x);
+                s.y = fmaf(gr[r], yv[r].y, s.y);
+                s.z = fmaf(gr[r], yv[r].z, s.z);
+                s.w = fmaf(gr[r], yv[r].w, s.w);
+            }
         }
     }
-    float s = Y[((int64_t)T * k + t) * d + i];
-    float yv[KMAX];
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r)
-        if (r < k) yv[r] = on[r] ? Y[(int64_t)pr[r] * d + i] : 0.f;
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r)
-        if (r < k && on[r]) s = fmaf(gr[r], yv[r], s);
-    a.out[gid] = s;
+    *(float4 *)(a.out + row) = s;
     if (a.x_next) {
-        const float xv = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[gid]) : ((const float *)a.x)[gid];
-        a.x_next[gid] = xv + s;
+        float4 xv;
+        if (XBF16) {
+            const uint2 q = *(const uint2 *)((const uint16_t *)a.x + row);
+            xv = make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
+                             __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
+        } else {
+            xv = *(const float4 *)((const float *)a.x + row);
+        }
+        *(float4 *)(a.x_next + row) = make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w);
     }
 }
 
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s) {
-    const int64_t n = (int64_t)a.T * a.d;
-    const int blocks = (int)((n + 255) / 256);
+    const int blocks = a.T * ((a.d + CB_COLS - 1) / CB_COLS);
     if (a.x_is_bf16)
         hipLaunchKernelGGL(combine_kernel<1>, dim3(blocks), dim3(256), 0, s, a);
     else

@@ -116,6 +116,8 @@ struct LayerArgs {
     int32_t *perm;       // [T*k]
     int32_t *pos;        // [T*k]
     float *inv_rms;      // [T]
+    int32_t *bcnt;       // [T/256 blocks][E] per-block expert counts, then first slots (larger T)
+    int32_t *bmiss;      // [T/256 blocks] per-block miss counts, then first miss-list entries
     WorkItem *items;     // work list
     int32_t *n_items;    // [1]
     uint32_t *counter;   // self-resetting arrival counter
@@ -159,6 +161,7 @@ hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s);
+int route_perm_blocks(int T);
 hipError_t launch_gemv_down(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemv_down_rows(const LayerArgs &a, hipStream_t s);
 bool down_rows_fits(int T, int k, int f);

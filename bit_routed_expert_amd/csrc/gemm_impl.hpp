@@ -29,13 +29,9 @@
 // 3-bit format; the low and high pairs of words A and B in the 2-bit
 // format), each group in nibble order [0,4,1,5,2,6,3,7].
 #pragma once
-#include "common.hpp"
+#include "mfma.hpp"
 
 namespace strata {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GM_NM = GEMM_BM / 32;   // 32-row token subtiles per tile
 constexpr int GSUB = 64;              // K positions per LDS stage
@@ -121,19 +117,10 @@ template <> struct Dec<2> {
     }
 };
 
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // byte offset of the 32-column unit U of row r in a packed [out][in] matrix
 template <int BITS> __device__ __forceinline__ int64_t unit_off(int r, int U, int in) {
     constexpr int UB = BITS == 3 ? 12 : 8;
     return ((((int64_t)(r >> 4) * (in >> 7) + (U >> 2)) * 16 + (r & 15)) * 4 + (U & 3)) * UB;
-}
-
-__device__ __forceinline__ uint16_t f2bf(float v) {   // round to nearest even (finite inputs)
-    const uint32_t u = __float_as_uint(v);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 // Staged A row m of the block, logical 16-byte chunk c (0..7).

@@ -8,6 +8,7 @@
 // section 二).  Logits are fp32; top-k is ordered by (logit desc, index asc);
 // gates are the softmax renormalised over the k picks.
 #include "routing.hpp"
+#include "mfma.hpp"
 
 namespace strata {
 
@@ -147,62 +148,135 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
     small_route_write(a, L);
 }
 
-// Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e], fp32,
-// 64x64 output tile per block, 16x16 threads with 4x4 outputs each.  Each
-// 32-column slab is summed on its own and the slab sums are added with
-// compensated (Kahan) summation, so the error stays near one fp32 rounding
-// of the logit instead of growing with d.
-__global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
-    __shared__ float xs[32][65];
-    __shared__ float ws[32][65];
-    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-    const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
-    const int d = a.d;
-    float acc[4][4] = {}, comp[4][4] = {};
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-            int r = i / 32, c = i % 32;
-            int t = t0 + r, e = e0 + r;
-            float xv = 0.f;
-            if (t < a.T) {
-                size_t o = (size_t)t * d + k0 + c;
-                xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+// Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e] on the bf16
+// matrix cores.  Wr (fp32) is split into three bf16 pieces, exactly; x is
+// one piece when it is bf16, else three (products of pieces below 2^-32 of
+// the leading one are dropped).  Every product is exact in fp32; each
+// 256-column block is summed on its own and the block sums are added with
+// compensated (Kahan) summation, so the logit error stays near one fp32
+// rounding.  Block tile 128 tokens x 64 experts; wave w owns tokens
+// 32*w .. +32 against all 64 experts (two 32x32 MFMA tiles).
+constexpr int RT_T = 128, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
+
+template <int PX>
+__global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[PX][RT_T * RT_RS];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[3][RT_E * RT_RS];
+    const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int t0 = blockIdx.y * RT_T, e0 = blockIdx.x * RT_E;
+    const int d = a.d, T = a.T, E = a.E;
+    // staging: x rows th/2 (16 columns each), Wr rows th/4 (8 columns each)
+    const int xr = th >> 1, xc = (th & 1) * 16;
+    const int wr = th >> 2, wc = (th & 3) * 8;
+    const int64_t xoff = (int64_t)min(t0 + xr, T - 1) * d + xc;
+    const float *wrow = a.Wr + (int64_t)min(e0 + wr, E - 1) * d + wc;
+    const bool wvalid = e0 + wr < E;
+    float xv[16], wv8[8];
+    auto load = [&](int k0) __attribute__((always_inline)) {
+        if (a.x_is_bf16) {
+            const uint4 *p = (const uint4 *)((const uint16_t *)a.x + xoff + k0);
+            const uint4 q0 = p[0], q1 = p[1];
+            const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                xv[2 * j] = __uint_as_float(w[j] << 16);
+                xv[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
             }
-            xs[c][r] = xv;
-            ws[c][r] = (e < a.E) ? a.Wr[(size_t)e * d + k0 + c] : 0.f;
-        }
-        __syncthreads();
-        float part[4][4] = {};
-#pragma unroll 8
-        for (int c = 0; c < 32; ++c) {
-            float xv[4], wv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { xv[i] = xs[c][ty + 16 * i]; wv[i] = ws[c][tx + 16 * i]; }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) part[i][j] = fmaf(xv[i], wv[j], part[i][j]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        } else {
+            const float4 *p = (const float4 *)((const float *)a.x + xoff + k0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float y = part[i][j] - comp[i][j];
-                const float t = acc[i][j] + y;
-                comp[i][j] = (t - acc[i][j]) - y;
-                acc[i][j] = t;
+                const float4 q = p[j];
+                xv[4 * j] = q.x; xv[4 * j + 1] = q.y; xv[4 * j + 2] = q.z; xv[4 * j + 3] = q.w;
             }
+        }
+        const float4 w0 = *(const float4 *)(wrow + k0), w1 = *(const float4 *)(wrow + k0 + 4);
+        wv8[0] = w0.x; wv8[1] = w0.y; wv8[2] = w0.z; wv8[3] = w0.w;
+        wv8[4] = w1.x; wv8[5] = w1.y; wv8[6] = w1.z; wv8[7] = w1.w;
+    };
+    f32x16_t P[2], acc[2], comp[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) P[j][v] = acc[j][v] = comp[j][v] = 0.f;
+    load(0);
+    for (int k0 = 0; k0 < d; k0 += RT_K) {
         __syncthreads();
+        {   // pieces into LDS
+            uint16_t hx[PX][16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (PX == 1) hx[0][j] = (uint16_t)(__float_as_uint(xv[j]) >> 16);
+                else split3(xv[j], hx[0][j], hx[PX > 1 ? 1 : 0][j], hx[PX > 2 ? 2 : 0][j]);
+            }
+#pragma unroll
+            for (int p = 0; p < PX; ++p) {
+                uint32_t w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) w[j] = (uint32_t)hx[p][2 * j] | ((uint32_t)hx[p][2 * j + 1] << 16);
+                uint4 *dst = (uint4 *)(xs[p] + xr * RT_RS + xc);
+                dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+            uint16_t hw[3][8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) split3(wvalid ? wv8[j] : 0.f, hw[0][j], hw[1][j], hw[2][j]);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = (uint32_t)hw[q][2 * j] | ((uint32_t)hw[q][2 * j + 1] << 16);
+                *(uint4 *)(ws[q] + wr * RT_RS + wc) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        __syncthreads();
+        if (k0 + RT_K < d) load(k0 + RT_K);
+#pragma unroll
+        for (int kk = 0; kk < RT_K; kk += 16) {
+            bf16x8_t A[PX], B[2][3];
+#pragma unroll
+            for (int p = 0; p < PX; ++p)
+                A[p] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(xs[p] + (wv * 32 + n) * RT_RS + kk + 8 * h));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    B[j][q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(ws[q] + (j * 32 + n) * RT_RS + kk + 8 * h));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                P[j] = mfma(A[0], B[j][0], P[j]);
+                P[j] = mfma(A[0], B[j][1], P[j]);
+                P[j] = mfma(A[0], B[j][2], P[j]);
+                if (PX == 3) {
+                    P[j] = mfma(A[PX > 1 ? 1 : 0], B[j][0], P[j]);
+                    P[j] = mfma(A[PX > 1 ? 1 : 0], B[j][1], P[j]);
+                    P[j] = mfma(A[PX > 2 ? 2 : 0], B[j][0], P[j]);
+                }
+            }
+        }
+        if (((k0 + RT_K) & 255) == 0 || k0 + RT_K >= d) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float y = P[j][v] - comp[j][v];
+                    const float t = acc[j][v] + y;
+                    comp[j][v] = (t - acc[j][v]) - y;
+                    acc[j][v] = t;
+                    P[j][v] = 0.f;
+                }
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int t = t0 + ty + 16 * i;
-        if (t >= a.T) continue;
-        float inv = a.inv_rms[t];
+    for (int j = 0; j < 2; ++j) {
+        const int e = e0 + j * 32 + n;
+        if (e >= E) continue;
+        const float b = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int e = e0 + tx + 16 * j;
-            if (e < a.E) a.z[(size_t)t * a.E + e] = acc[i][j] * inv + (a.bias ? a.bias[e] : 0.f);
+        for (int v = 0; v < 16; ++v) {
+            const int t = t0 + wv * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (t < T) a.z[(int64_t)t * E + e] = acc[j][v] * a.inv_rms[t] + b;
         }
     }
 }
@@ -216,128 +290,125 @@ __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
               nullptr, nullptr);
 }
 
-// Any T: one block of 1024 threads.  Counts by LDS atomics (integer, so the
-// result is order independent), exclusive scan, then a stable scatter over
-// 512-token windows: within a window each expert's picks are marked in a
-// bitmap and a pick's rank is the number of marked earlier tokens.
-// Window of PW tokens (512, or 256 when E > 512 so the bitmaps fit in LDS).
-__global__ __launch_bounds__(1024) void route_permute_kernel(LayerArgs a, int PW, int tile) {
-    extern __shared__ int32_t sh[];
-    const int th = threadIdx.x, nth = 1024;
-    const int E = a.E, k = a.k, T = a.T;
-    const int64_t n = (int64_t)T * k;
-    int32_t *hist = sh;                 // [E]
-    int32_t *run = sh + E;              // [E] running slot per expert
-    int32_t *scan = sh + 2 * E;         // [1024]
-    uint32_t *bm = (uint32_t *)(sh + 2 * E + 1024);  // [E][PW/32]
-    const int BW = PW / 32;
-    for (int e = th; e < E; e += nth) hist[e] = 0;
+// ------------------------------------------------ permutation (larger T)
+// Slots are ordered by (expert asc, token asc): three passes over blocks
+// of PERM_T tokens.  route_count: per-block expert histogram and miss
+// count; route_scan: totals, offsets, each block's first slot per expert,
+// each block's first miss-list entry, and the work list; route_scatter:
+// the stable rank of every pick inside its block (per-expert token
+// bitmaps), perm/pos and the miss list in (t, r) order.
+constexpr int PERM_T = 256;
+
+__global__ __launch_bounds__(256) void route_count_kernel(LayerArgs a) {
+    __shared__ int hist[1024];
+    __shared__ int tmp[16];
+    const int th = threadIdx.x, b = blockIdx.x, E = a.E, k = a.k;
+    const int t0 = b * PERM_T, nt = min(PERM_T, a.T - t0);
+    for (int e = th; e < E; e += 256) hist[e] = 0;
     __syncthreads();
-    for (int64_t i = th; i < n; i += nth) atomicAdd(&hist[a.idx[i]], 1);
-    __syncthreads();
-    // exclusive scan over experts (E <= 1024, one per thread)
-    int v = th < E ? hist[th] : 0;
-    scan[th] = v;
-    __syncthreads();
-    for (int o = 1; o < nth; o <<= 1) {
-        int add = th >= o ? scan[th - o] : 0;
-        __syncthreads();
-        scan[th] += add;
-        __syncthreads();
+    int nmiss = 0;
+    for (int i = th; i < nt * k; i += 256) {
+        const int e = a.idx[(int64_t)t0 * k + i];
+        atomicAdd(&hist[e], 1);
+        nmiss += is_resident(a.mask, e) ? 0 : 1;
     }
-    int excl = scan[th] - v;
+    __syncthreads();
+    for (int e = th; e < E; e += 256) a.bcnt[(int64_t)b * E + e] = hist[e];
+    int tot;
+    block_excl_scan(nmiss, tmp, &tot);
+    if (th == 0) a.bmiss[b] = tot;
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(LayerArgs a, int nb, int tile) {
+    __shared__ int tmp[16];
+    const int th = threadIdx.x, E = a.E, T = a.T;
+    const int64_t n = (int64_t)T * a.k;
+    int c = 0;
+    if (th < E)
+        for (int b = 0; b < nb; ++b) c += a.bcnt[(int64_t)b * E + th];
+    int tot;
+    const int off = block_excl_scan(c, tmp, &tot);
     if (th < E) {
-        run[th] = excl;
-        a.counts[th] = v;
-        a.offsets[th] = excl;
-        if (a.u_counts) a.u_counts[th] = v;
-        if (a.u_offsets) a.u_offsets[th] = excl;
-    }
-    if (th == nth - 1) {
-        a.offsets[E] = scan[th];
-        if (a.u_offsets) a.u_offsets[E] = scan[th];
-    }
-    __syncthreads();
-    for (int w0 = 0; w0 < T; w0 += PW) {
-        for (int i = th; i < E * BW; i += nth) bm[i] = 0;
-        __syncthreads();
-        int wn = min(PW, T - w0);
-        for (int i = th; i < wn * k; i += nth) {
-            int tl = i / k;
-            int e = a.idx[(int64_t)(w0 + tl) * k + i % k];
-            atomicOr(&bm[e * BW + tl / 32], 1u << (tl % 32));
+        a.counts[th] = c;
+        a.offsets[th] = off;
+        if (a.u_counts) a.u_counts[th] = c;
+        if (a.u_offsets) a.u_offsets[th] = off;
+        int run = off;
+        for (int b = 0; b < nb; ++b) {   // in place: count -> first slot of the block
+            const int v = a.bcnt[(int64_t)b * E + th];
+            a.bcnt[(int64_t)b * E + th] = run;
+            run += v;
         }
-        __syncthreads();
-        for (int i = th; i < wn * k; i += nth) {
-            int tl = i / k;
-            int64_t gi = (int64_t)(w0 + tl) * k + i % k;
-            int e = a.idx[gi];
-            int rank = 0;
-            for (int w = 0; w < tl / 32; ++w) rank += __popc(bm[e * BW + w]);
-            rank += __popc(bm[e * BW + tl / 32] & ((1u << (tl % 32)) - 1u));
-            int slot = run[e] + rank;
-            a.perm[slot] = (int32_t)gi;
-            a.pos[gi] = slot;
-            if (a.u_perm) a.u_perm[slot] = (int32_t)gi;
-            if (a.u_pos) a.u_pos[gi] = slot;
-        }
-        __syncthreads();
-        for (int e = th; e < E; e += nth) {
-            int c = 0;
-            for (int w = 0; w < BW; ++w) c += __popc(bm[e * BW + w]);
-            run[e] += c;
-        }
-        __syncthreads();
     }
-    // miss list in (t, r) order
-    int total = 0;
-    for (int64_t b0 = 0; b0 < n; b0 += nth) {
-        int64_t i = b0 + th;
-        int e = i < n ? a.idx[i] : 0;
-        int f = (i < n && !is_resident(a.mask, e)) ? 1 : 0;
-        scan[th] = f;
-        __syncthreads();
-        for (int o = 1; o < nth; o <<= 1) {
-            int add = th >= o ? scan[th - o] : 0;
-            __syncthreads();
-            scan[th] += add;
-            __syncthreads();
-        }
-        int p = total + scan[th] - f;
-        if (f && a.miss_te && p < a.miss_cap) {
-            a.miss_te[2 * (int64_t)p] = (int32_t)(i / k);
-            a.miss_te[2 * (int64_t)p + 1] = e;
-            a.miss_w[p] = a.gate[i];
-        }
-        total += scan[nth - 1];
-        __syncthreads();
-    }
-    if (th == 0 && a.miss_count) *a.miss_count = total;
-    // work list: ceil(count/tile) items per resident expert with picks, then the shared expert
-    int ni = (th < E && is_resident(a.mask, th)) ? (hist[th] + tile - 1) / tile : 0;
-    scan[th] = ni;
-    __syncthreads();
-    for (int o = 1; o < nth; o <<= 1) {
-        int add = th >= o ? scan[th - o] : 0;
-        __syncthreads();
-        scan[th] += add;
-        __syncthreads();
-    }
-    int base = scan[th] - ni;
-    if (th < E) {
-        int off = scan[th] - ni;  // item base
-        (void)off;
-        int s0 = run[th] - hist[th];  // run[] now holds offsets + counts
-        for (int j = 0; j < ni; ++j)
-            a.items[base + j] = WorkItem{th, s0 + j * tile, min(tile, hist[th] - j * tile)};
-    }
-    int nr = scan[nth - 1];
-    __syncthreads();
     if (th == 0) {
-        int c = nr;
-        for (int t0 = 0; t0 < T; t0 += tile)
-            a.items[c++] = WorkItem{E, (int32_t)(n + t0), min(tile, T - t0)};
-        *a.n_items = c;
+        a.offsets[E] = (int32_t)n;
+        if (a.u_offsets) a.u_offsets[E] = (int32_t)n;
+    }
+    // first miss-list entry of every block
+    int mbase = 0;
+    for (int b0 = 0; b0 < nb; b0 += 1024) {
+        const int b = b0 + th;
+        const int v = b < nb ? a.bmiss[b] : 0;
+        int sum;
+        const int ex = block_excl_scan(v, tmp, &sum);
+        __syncthreads();
+        if (b < nb) a.bmiss[b] = mbase + ex;
+        mbase += sum;
+    }
+    if (th == 0 && a.miss_count) *a.miss_count = mbase;
+    // work list: ceil(count/tile) items per resident expert with picks, then the shared expert
+    const int ni = (th < E && is_resident(a.mask, th)) ? (c + tile - 1) / tile : 0;
+    int nr;
+    const int base = block_excl_scan(ni, tmp, &nr);
+    for (int j = 0; j < ni; ++j) a.items[base + j] = WorkItem{th, off + j * tile, min(tile, c - j * tile)};
+    const int ns = (T + tile - 1) / tile;
+    for (int j = th; j < ns; j += 1024)
+        a.items[nr + j] = WorkItem{E, (int32_t)(n + (int64_t)j * tile), min(tile, T - j * tile)};
+    if (th == 0) *a.n_items = nr + ns;
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(LayerArgs a) {
+    extern __shared__ uint32_t lds_u[];
+    constexpr int BW = PERM_T / 32;
+    const int th = threadIdx.x, b = blockIdx.x, E = a.E, k = a.k;
+    uint32_t *bm = lds_u;                           // [E][BW] token bitmaps
+    int *base = (int *)(lds_u + E * BW);            // [E] first slot of this block
+    int *tmp = base + E;                            // [16]
+    const int t0 = b * PERM_T, nt = min(PERM_T, a.T - t0);
+    for (int i = th; i < E * BW; i += 256) bm[i] = 0;
+    for (int e = th; e < E; e += 256) base[e] = a.bcnt[(int64_t)b * E + e];
+    __syncthreads();
+    const int64_t g0 = (int64_t)t0 * k;
+    for (int i = th; i < nt * k; i += 256) {
+        const int tl = i / k, e = a.idx[g0 + i];
+        atomicOr(&bm[e * BW + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    for (int i = th; i < nt * k; i += 256) {
+        const int tl = i / k, e = a.idx[g0 + i];
+        int rank = __popc(bm[e * BW + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
+        for (int w = 0; w < (tl >> 5); ++w) rank += __popc(bm[e * BW + w]);
+        const int slot = base[e] + rank;
+        a.perm[slot] = (int32_t)(g0 + i);
+        a.pos[g0 + i] = slot;
+        if (a.u_perm) a.u_perm[slot] = (int32_t)(g0 + i);
+        if (a.u_pos) a.u_pos[g0 + i] = slot;
+    }
+    // miss list entries of this block, in pick order (t asc, r asc)
+    int mrun = a.bmiss[b];
+    for (int i0 = 0; i0 < nt * k; i0 += 256) {
+        const int i = i0 + th;
+        const int e = i < nt * k ? a.idx[g0 + i] : 0;
+        const int f = (i < nt * k && !is_resident(a.mask, e)) ? 1 : 0;
+        int sum;
+        const int p = mrun + block_excl_scan(f, tmp, &sum);
+        if (f && a.miss_te && p < a.miss_cap) {
+            a.miss_te[2 * (int64_t)p] = (int32_t)((g0 + i) / k);
+            a.miss_te[2 * (int64_t)p + 1] = e;
+            a.miss_w[p] = a.gate[g0 + i];
+        }
+        mrun += sum;
+        __syncthreads();
     }
 }
 
@@ -361,7 +432,12 @@ hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(route_logits_kernel, dim3((a.E + 63) / 64, (a.T + 63) / 64), dim3(256), 0, s, a);
+    const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T);
+    if (a.d % RT_K) return hipErrorInvalidValue;
+    if (a.x_is_bf16)
+        hipLaunchKernelGGL(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(route_logits_mfma_kernel<3>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -370,11 +446,16 @@ hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+int route_perm_blocks(int T) { return (T + PERM_T - 1) / PERM_T; }
+
 hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s) {
-    const int pw = a.E <= 512 ? 512 : 256;
-    const size_t lds = sizeof(int32_t) * (size_t)(2 * a.E + 1024) + sizeof(uint32_t) * (size_t)a.E * (pw / 32);
+    const int nb = route_perm_blocks(a.T);
+    if (a.E > 1024) return hipErrorInvalidValue;
+    const size_t lds = 4 * ((size_t)a.E * (PERM_T / 32) + a.E + 16);
     if (lds > LDS_LIMIT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), lds, s, a, pw, tile);
+    hipLaunchKernelGGL(route_count_kernel, dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, a, nb, tile);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
