@@ -14,8 +14,11 @@ extern template hipError_t down_rows_launch<2>(const LayerArgs &, hipStream_t);
 bool gemv_supported(int d, int f, int bits) { return gemv_supported_impl(d, f, bits); }
 
 bool down_rows_fits(int T, int k, int f) {
-    const int R = 64 / pick_slices(f);
-    return T <= CHUNK_TOK && down_rows_lds(T, k, f, R, nt_round(ntmax_for(T))) <= LDS_LIMIT;
+    const int R = 64 / unit_slices(f, 8);
+    const int nt = nt_round(ntmax_for(T));
+    if (T == 1) return k + 1 <= 12 && 4 * (size_t)down_one_lds_words(k, f, 64 / unit_slices(f, 8)) <= LDS_LIMIT;
+    const int nw = down_rows_waves(T, k, f, R, nt);
+    return T <= CHUNK_TOK && down_rows_lds(T, k, f, R, nt, nw) <= LDS_LIMIT;
 }
 
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s) {

@@ -17,32 +17,35 @@
 //     exact correction sum((c - c0) X) = sum(c X) - c0 * sum(X);
 //   * the fp16 block scale and 2^-E are applied once per (row, group, token).
 // Lane mapping: a wave covers R rows x S = 64/R column slices; lane
-// (row r, slice s) reads its row's 4 units (48 or 32 bytes) of each
-// 128-column group in its slice with 16-byte loads and keeps per-token
-// partial sums; the S slices are summed with cross-lane adds.
+// (row r, slice s) reads up to 4 consecutive 32-column units of its row
+// (one 128-column group is read with 16-byte loads) and keeps per-token
+// partial sums; the S slices are summed with cross-lane adds.  Every
+// kernel uses the same slicing for a given matrix width, so a token's
+// result does not depend on how many tokens share the call.
 //
 // Kernels:
-//   gate/up: a block owns 2R rows j of gate and the same rows of up for one
+//   gate/up: a block owns 32 rows j of gate and the same rows of up for one
 //     work item (<= 8 tokens of one expert), so it forms h = silu(g) * u and
 //     writes h already quantised (digit planes per 32-column group).
 //   down, T <= 8: a block owns R rows of Wd for every work item, so the
 //     weighted combine with the shared expert and the residual add happen in
-//     the block (fixed order, no cross-block step).
+//     the block (fixed order, no cross-block step); one token takes one wave
+//     per work item.
 //   down, larger T: a block per (work item, 2R-row tile) writes expert
 //     outputs; the combine kernel sums them.
 #pragma once
+#include <algorithm>
+
 #include "routing.hpp"
 
 namespace strata {
 
-constexpr int MAXQ = 4;           // 128-column groups per lane slice
 constexpr int HGROUP_UNITS = 1;   // h is quantised per 32 columns
 constexpr int XGROUP_UNITS = 8;   // the layer input per 256 columns
 constexpr int MAX_HUNITS = 24;    // f <= 768 on this path
 
 template <int BITS> struct Fmt {
     static constexpr int UB = BITS == 3 ? 12 : 8;  // bytes per 32-code unit
-    static constexpr int DW = UB;                  // dwords per 128-column group (4 units)
     static constexpr int C2 = BITS == 3 ? 7 : 3;   // 2 * code offset
 };
 
@@ -77,50 +80,66 @@ __device__ __forceinline__ int dig_off(int U, int units_per_slice) {
     return U * XPLANES * 4 + (U / units_per_slice) * 4;
 }
 
-// Codes and block scales of rows [row0, row0+R) of one packed matrix
-// [out][in], for this lane's slice.
-template <int BITS> struct WTile {
-    uint32_t w[MAXQ][Fmt<BITS>::DW];
-    uint32_t sc[MAXQ];  // fp16 scale bits per 128-column group (32-bit slots: packing
-                        // 16-bit loads would stall the load stream)
+// Unit-granular tile for the decode kernels: lane (row r = lane % R, slice
+// s = lane / R) holds units [s*upl, (s+1)*upl) of row row0 + r (upl <= 8;
+// aligned runs of 4 units are 128-column groups, read with 16-byte loads),
+// and each unit's fp16 block scale.
+constexpr int UPL_MAX = 8;
+template <int BITS> struct UTile {
+    uint32_t w[UPL_MAX][Fmt<BITS>::UB / 4];
+    uint32_t sc[UPL_MAX];
 
-    __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, const uint16_t *__restrict__ msc,
-                                         int in, int row0, int R) {
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, const uint16_t *__restrict__ msc, int in,
+                                         int row0, int R, int upl) {
         const int lane = threadIdx.x & 63;
-        const int S = 64 / R, Q = in / 128, QPS = Q / S;
-        const int r = row0 + lane % R, s = lane / R;
+        const int r = row0 + lane % R, U0 = (lane / R) * upl;
         constexpr int UB = Fmt<BITS>::UB;
-        const uint8_t *base = mat + ((size_t)((r / 16) * Q + s * QPS) * 16 + (r % 16)) * 4 * UB;
+        const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
+        if (upl % 4 == 0) {   // aligned groups: 48 or 32 contiguous bytes each
 #pragma unroll
-        for (int qq = 0; qq < MAXQ; ++qq) {
-            if (qq < QPS) {
-                const uint4 *p = (const uint4 *)(base + (size_t)qq * 16 * 4 * UB);
+            for (int gq = 0; gq < UPL_MAX / 4; ++gq) {
+                if (4 * gq < upl) {
+                    const uint4 *p = (const uint4 *)(mat + rbase + (int64_t)((U0 >> 2) + gq) * 64 * UB);
 #pragma unroll
-                for (int i = 0; i < Fmt<BITS>::DW / 4; ++i) {
-                    const uint4 v = p[i];
-                    w[qq][4 * i] = v.x;
-                    w[qq][4 * i + 1] = v.y;
-                    w[qq][4 * i + 2] = v.z;
-                    w[qq][4 * i + 3] = v.w;
+                    for (int i = 0; i < UB / 4; ++i) {
+                        const uint4 v = p[i];
+                        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            w[4 * gq + (4 * i + c) / (UB / 4)][(4 * i + c) % (UB / 4)] = q[c];
+                    }
                 }
-                sc[qq] = (uint32_t)msc[((long)r * in + (s * QPS + qq) * 128) / 256];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < UPL_MAX; ++u) {
+                if (u < upl) {
+                    const int U = U0 + u;
+                    const uint32_t *p = (const uint32_t *)(mat + rbase + ((int64_t)(U >> 2) * 64 + (U & 3)) * UB);
+#pragma unroll
+                    for (int i = 0; i < UB / 4; ++i) w[u][i] = p[i];
+                }
             }
         }
+#pragma unroll
+        for (int u = 0; u < UPL_MAX; ++u)
+            if (u < upl) sc[u] = msc[((int64_t)r * in + 32 * (U0 + u)) >> 8];
     }
 };
 
-// Row sums of a loaded tile against NT tokens whose digit planes sit in LDS
-// (dig + t*dstride, laid out by dig_off), with per-(token, unit) digit sums
-// usum[t*ustride + U] and per-(token, group) scales gscl[t*gstride + U/upg].
+// Row sums of a UTile against NT tokens (digit planes in LDS at dig +
+// tmap[t]*dstride, laid out by dig_off with upl units per slice; unit sums
+// usum[tmap[t]*ustride + U]; activation scales gscl[tmap[t]*gstride + U/upg]).
+// Partial sums are flushed into res every `period` units (a period never
+// spans two weight blocks or two activation groups) and at the slice end.
 // res[t] is complete in lanes with s == 0 (lane < R).
 template <int BITS, int NT>
-__device__ __forceinline__ void tile_compute(const WTile<BITS> &wt, int in, int R, const uint32_t *__restrict__ dig,
-                                             int dstride, const int *__restrict__ usum, int ustride,
-                                             const float *__restrict__ gscl, int gstride, int upg, float res[NT]) {
+__device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int upl, int period,
+                                              const uint32_t *__restrict__ dig, int dstride,
+                                              const int *__restrict__ usum, int ustride, const float *__restrict__ gscl,
+                                              int gstride, int upg, const int *tmap, float res[NT]) {
     const int lane = threadIdx.x & 63;
-    const int S = 64 / R, Q = in / 128, QPS = Q / S;
-    const int s = lane / R;
-    const int ups = QPS * 4;
+    const int U0 = (lane / R) * upl;
     int acc[NT][XPLANES];
     int sx[NT];
 #pragma unroll
@@ -131,42 +150,38 @@ __device__ __forceinline__ void tile_compute(const WTile<BITS> &wt, int in, int 
         for (int p = 0; p < XPLANES; ++p) acc[t][p] = 0;
     }
 #pragma unroll
-    for (int qq = 0; qq < MAXQ; ++qq) {
-        if (qq < QPS) {
-            const int q = s * QPS + qq;
-            const float scl = 0.5f * half_to_float((uint16_t)wt.sc[qq]);
+    for (int u = 0; u < UPL_MAX; ++u) {
+        if (u < upl) {
+            const int U = U0 + u;
+            uint32_t N[4];
+            unit_nibbles<BITS>(wt.w[u], N);
+            const int off = dig_off(U, upl);
 #pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-                const int U = q * 4 + uu;
-                uint32_t N[4];
-                unit_nibbles<BITS>(&wt.w[qq][uu * Fmt<BITS>::UB / 4], N);
-                const int off = dig_off(U, ups);
+            for (int t = 0; t < NT; ++t) {
+                const int tt = tmap ? tmap[t] : t;
+                const uint4 *dp = (const uint4 *)(dig + tt * dstride + off);
+#pragma unroll
+                for (int p = 0; p < XPLANES; ++p) {
+                    const uint4 dv = dp[p];
+                    int a_ = acc[t][p];
+                    a_ = __builtin_amdgcn_sdot8((int)N[0], (int)dv.x, a_, false);
+                    a_ = __builtin_amdgcn_sdot8((int)N[1], (int)dv.y, a_, false);
+                    a_ = __builtin_amdgcn_sdot8((int)N[2], (int)dv.z, a_, false);
+                    a_ = __builtin_amdgcn_sdot8((int)N[3], (int)dv.w, a_, false);
+                    acc[t][p] = a_;
+                }
+                sx[t] += usum[tt * ustride + U];
+            }
+            if (u == upl - 1 || (U + 1) % period == 0) {
+                const float scl = 0.5f * half_to_float((uint16_t)wt.sc[u]);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const uint4 *dp = (const uint4 *)(dig + t * dstride + off);
+                    const int tt = tmap ? tmap[t] : t;
+                    const float v = digits_value(acc[t], Fmt<BITS>::C2, sx[t]);
+                    res[t] = fmaf(v, scl * gscl[tt * gstride + U / upg], res[t]);
+                    sx[t] = 0;
 #pragma unroll
-                    for (int p = 0; p < XPLANES; ++p) {
-                        const uint4 dv = dp[p];
-                        int a_ = acc[t][p];
-                        a_ = __builtin_amdgcn_sdot8((int)N[0], (int)dv.x, a_, false);
-                        a_ = __builtin_amdgcn_sdot8((int)N[1], (int)dv.y, a_, false);
-                        a_ = __builtin_amdgcn_sdot8((int)N[2], (int)dv.z, a_, false);
-                        a_ = __builtin_amdgcn_sdot8((int)N[3], (int)dv.w, a_, false);
-                        acc[t][p] = a_;
-                    }
-                    sx[t] += usum[t * ustride + U];
-                }
-                // flush at the end of a scale group or of the slice (a 128-column
-                // group never straddles two weight blocks)
-                if ((U + 1) % upg == 0 || (qq == QPS - 1 && uu == 3)) {
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const float v = digits_value(acc[t], Fmt<BITS>::C2, sx[t]);
-                        res[t] = fmaf(v, scl * gscl[t * gstride + U / upg], res[t]);
-                        sx[t] = 0;
-#pragma unroll
-                        for (int p = 0; p < XPLANES; ++p) acc[t][p] = 0;
-                    }
+                    for (int p = 0; p < XPLANES; ++p) acc[t][p] = 0;
                 }
             }
         }
@@ -175,6 +190,23 @@ __device__ __forceinline__ void tile_compute(const WTile<BITS> &wt, int in, int 
 #pragma unroll
         for (int t = 0; t < NT; ++t) res[t] += __shfl_xor(res[t], o, WAVE);
     }
+}
+
+// Lane slices of the decode kernels for a matrix with `in` columns: the most
+// slices (a power of two up to smax) that split its 32-column units evenly
+// with at most UPL_MAX units each (and whole groups once a slice has 4 or
+// more units); 0 if none.
+__host__ __device__ inline int unit_slices(int in, int smax) {
+    const int units = in / 32;
+    for (int S = smax; S >= 1; S >>= 1)
+        if (units % S == 0 && units / S <= UPL_MAX && (units / S < 4 || (units / S) % 4 == 0)) return S;
+    return 0;
+}
+// Flush period (units): within one weight block (8 units, or 4 when the row
+// length is an odd multiple of 128 columns) and one activation group.
+__host__ __device__ inline int unit_period(int in, int upg) {
+    const int wp = (in % 256) ? 4 : 8;
+    return upg < wp ? upg : wp;
 }
 
 // Quantise 8 consecutive values with exponent E into one word per digit
@@ -201,75 +233,88 @@ __device__ __forceinline__ int slot_token(const LayerArgs &a, const WorkItem &it
 }
 
 // ---------------------------------------------------------- gate and up
-// Block = 4 waves: waves 0,1 compute gate rows j0 .. j0+2R-1 (R each),
-// waves 2,3 the same rows of up.  Then h = silu(g) * u for those 2R rows and
-// the item's tokens, quantised per 32 columns, goes to hq/hsum/hscl.
+// LDS of the gate/up kernel: digit planes, unit sums and group scales of all
+// T tokens, then the gate/up results [2][NT][2R], then the routing state.
+struct GuLds {
+    int dstride, units, G;
+    uint32_t *dig;
+    int *sum;
+    float *scl;
+    float *gu;
+    __device__ GuLds(uint32_t *lds, int d, int R, int T, int NT) {
+        const int S = 64 / R;
+        units = d / 32;
+        G = (d + 255) / 256;
+        dstride = units * XPLANES * 4 + S * 4;
+        dig = lds;
+        sum = (int *)(lds + T * dstride);
+        scl = (float *)(sum + T * units);
+        gu = scl + T * G;
+    }
+};
+__host__ __device__ inline int gateup_lds_words(int d, int R, int T, int nt) {
+    const int S = 64 / R;
+    const int dstride = (d / 32) * XPLANES * 4 + S * 4;
+    return T * dstride + T * (d / 32) + T * ((d + 255) / 256) + 2 * nt * 32;
+}
+
+// Staging of every token's input digit planes into LDS by direct
+// global->LDS loads, one lane-slice run (ups units, contiguous in both
+// places) per load (two when a run exceeds 64 chunks), issued by the waves
+// that do not take a top-k so they overlap the routing.
+__device__ __forceinline__ void xstage_issue(const LayerArgs &a, const GuLds &g, int S, int ups) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, T = a.T, NW = blockDim.x >> 6;
+    const int w0 = T < NW ? T : NW - 1;   // first staging wave
+    if (wave < w0) return;
+    const int nw = NW - w0, chunks = ups * XPLANES;   // 16-byte chunks per run
+    const int per = (chunks + 63) / 64;
+    for (int job = wave - w0; job < T * S * per; job += nw) {
+        const int run = job / per, part = job % per, t = run / S, sl = run % S;
+        const int c = part * 64 + lane;
+        const uint32_t *src = a.xq + ((size_t)t * g.units + sl * ups) * XPLANES * 4 + 4 * (size_t)min(c, chunks - 1);
+        uint32_t *dst = g.dig + t * g.dstride + dig_off(sl * ups, ups) + 4 * part * 64;
+        if (c < chunks) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+}
+// Gate/up for the NT tokens toks[] of one work item: waves [0, NWM) take
+// gate rows j0 + R*w .. +R, waves [NWM, 2*NWM) the same rows of up (NWM =
+// 32 / R, so a block owns 32 columns of h).  Then h = silu(g) * u for those
+// 32 columns, quantised per 32 columns, goes to hq/hsum/hscl.
 template <int BITS, int NT>
 __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &it, const int *toks, int R,
-                                            int j0, uint32_t *lds) {
+                                            int j0, const GuLds &g) {
     const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
-    const int d = a.d, f = a.f;
-    const int m = wave >> 1;  // 0 gate, 1 up
-    const int row0 = j0 + (wave & 1) * R;
+    const int d = a.d, f = a.f, NWM = 32 / R;
+    const int m = wave / NWM;  // 0 gate, 1 up
+    const int row0 = j0 + (wave % NWM) * R;
+    const int upl = (d / 32) / (64 / R);
     const size_t mat_bytes = (size_t)d * f * BITS / 8;
     const size_t mat_blocks = (size_t)d * f / 256;
     const size_t mi = (size_t)it.expert * 3 + m;
-    WTile<BITS> wt;
-    wt.load(a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, row0, R);
-
-    // stage the tokens' digit planes, unit sums and group scales (every
-    // staging load of a pass is issued before any LDS write)
-    const int Q = d / 128, G = (d + 255) / 256, units = d / 32;
-    const int S = 64 / R, ups = (Q / S) * 4;
-    const int dstride = units * XPLANES * 4 + S * 4;
-    uint32_t *ldig = lds;
-    int *lsum = (int *)(lds + NT * dstride);
-    float *lscl = (float *)(lsum + NT * units);
-    float *gu = lscl + NT * G;  // [2][NT][2R]
-    const int n16 = units * XPLANES;  // uint4 per token
-    for (int base = 0; base < NT * n16; base += 256 * 4) {
-        uint4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = min(base + th + 256 * u, NT * n16 - 1), j = i / n16, q = i % n16;
-            v[u] = ((const uint4 *)(a.xq + (size_t)toks[j] * units * XPLANES * 4))[q];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + th + 256 * u;
-            if (i < NT * n16) {
-                const int j = i / n16, q = i % n16, U = q / XPLANES, p = q % XPLANES;
-                *(uint4 *)(ldig + j * dstride + dig_off(U, ups) + 4 * p) = v[u];
-            }
-        }
-    }
-    for (int q = th; q < NT * (units + G); q += 256) {
-        const int j = q / (units + G), i = q % (units + G);
-        if (i < units) lsum[j * units + i] = a.xsum[(size_t)toks[j] * units + i];
-        else lscl[j * G + (i - units)] = a.xscl[(size_t)toks[j] * G + (i - units)];
-    }
-    __syncthreads();
+    UTile<BITS> wt;
+    wt.load(a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, row0, R, upl);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
+    __syncthreads();                                  // every wave's staged digit planes visible
     float res[NT];
-    tile_compute<BITS, NT>(wt, d, R, ldig, dstride, lsum, units, lscl, G, XGROUP_UNITS, res);
-    const int hb = 2 * R;
+    utile_compute<BITS, NT>(wt, R, upl, unit_period(d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl, g.G,
+                            XGROUP_UNITS, toks, res);
     if (lane < R) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) gu[(m * NT + j) * hb + (wave & 1) * R + lane] = res[j];
+        for (int j = 0; j < NT; ++j) g.gu[(m * NT + j) * 32 + (wave % NWM) * R + lane] = res[j];
     }
     __syncthreads();
-    // h for NT tokens x hb columns: one chunk of 8 columns per lane of wave 0
+    // h for NT tokens x 32 columns: one chunk of 8 columns per lane of wave 0
     if (wave == 0) {
-        const int cpt = hb / 8;  // chunks per token
-        const int c = lane % cpt, j = lane / cpt;
+        const int c = lane & 3, j = lane >> 2;
         const bool valid = j < NT;
         const int jj = valid ? j : 0;
         float h[8];
         float mx = 0.f;
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-            const float g = gu[jj * hb + c * 8 + n];
-            const float u = gu[(NT + jj) * hb + c * 8 + n];
-            h[n] = valid ? g / (1.f + expf(-g)) * u : 0.f;
+            const float gv = g.gu[jj * 32 + c * 8 + n];
+            const float u = g.gu[(NT + jj) * 32 + c * 8 + n];
+            h[n] = valid ? gv / (1.f + expf(-gv)) * u : 0.f;
             mx = fmaxf(mx, fabsf(h[n]));
         }
         // a 32-column group is 4 consecutive lanes
@@ -282,22 +327,16 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
         sx += __shfl_xor(sx, 2, WAVE);
         if (valid) {
             const int slot = it.slot0 + j;
-            const int col = j0 + c * 8, U = col / 32, i = (col / 8) % 4;
+            const int U = j0 / 32;
             uint32_t *dst = a.hq + ((size_t)slot * (f / 32) + U) * (XPLANES * 4);
 #pragma unroll
-            for (int p = 0; p < XPLANES; ++p) dst[p * 4 + i] = word[p];
-            if (i == 0) {
+            for (int p = 0; p < XPLANES; ++p) dst[p * 4 + c] = word[p];
+            if (c == 0) {
                 a.hsum[(size_t)slot * (f / 32) + U] = sx;
                 a.hscl[(size_t)slot * (f / 32) + U] = ldexpf(1.f, -E);
             }
         }
     }
-}
-
-__host__ __device__ inline int gateup_lds_words(int d, int R, int nt) {
-    const int S = 64 / R;
-    const int dstride = (d / 32) * XPLANES * 4 + S * 4;
-    return nt * dstride + nt * (d / 32) + nt * ((d + 255) / 256) + 2 * nt * 2 * R;
 }
 
 #define NT_SWITCH(BODY)                                               \
@@ -313,25 +352,52 @@ __host__ __device__ inline int gateup_lds_words(int d, int R, int nt) {
         default: break;                                               \
     }
 
-
-// T <= 8: every block takes the top-k of the T tokens itself from the
-// router logits (a few KB), derives its own work item and runs it; the last
-// block writes the routing outputs and the work list instead.
+// T <= 8: every block (2 * 32/R waves, 32 columns of h) takes the top-k of
+// the T tokens itself from the router logits (a few KB) while its input
+// digit planes, unit sums and group scales load, derives its own work item
+// and runs it; the last block writes the routing outputs and the work list
+// instead.
 template <int BITS, int NTMAX>
-__global__ __launch_bounds__(256) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_gateup_small_kernel(
+    LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
+    const GuLds g(lds, a.d, R, a.T, NTMAX);
     const SmallRoute L(lds + route_off, a.E);
-    small_route_compute(a, L);
+    const int S = 64 / R, upl = (a.d / 32) / S;
     if (blockIdx.x == gridDim.x - 1) {
+        small_route_compute(a, L, a.z, a.inv_rms);
         small_route_write(a, L);
         return;
     }
-    const int wg_per_item = a.f / (2 * R);
+    xstage_issue(a, g, S, upl);
+    // unit sums and group scales into registers now, LDS after the routing
+    const int per = g.units + g.G, nq = a.T * per;
+    int qv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
+        qv[u] = q < nq ? (i < g.units ? a.xsum[(size_t)j * g.units + i] : __float_as_int(a.xscl[(size_t)j * g.G + i - g.units])) : 0;
+    }
+    small_route_compute(a, L, a.z, a.inv_rms);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
+        if (q < nq) {
+            if (i < g.units) g.sum[j * g.units + i] = qv[u];
+            else g.scl[j * g.G + i - g.units] = __int_as_float(qv[u]);
+        }
+    }
+    for (int q = threadIdx.x + 2 * blockDim.x; q < nq; q += blockDim.x) {   // large d
+        const int j = q / per, i = q % per;
+        if (i < g.units) g.sum[j * g.units + i] = a.xsum[(size_t)j * g.units + i];
+        else g.scl[j * g.G + i - g.units] = a.xscl[(size_t)j * g.G + i - g.units];
+    }
+    const int wg_per_item = a.f / 32;
     WorkItem it;
     int toks[CHUNK_TOK];
     if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, toks)) return;
-    const int j0 = (blockIdx.x % wg_per_item) * 2 * R;
-#define GU(n) gateup_body<BITS, n>(a, it, toks, R, j0, lds)
+    const int j0 = (blockIdx.x % wg_per_item) * 32;
+#define GU(n) gateup_body<BITS, n>(a, it, toks, R, j0, g)
     NT_SWITCH(GU)
 #undef GU
 }
@@ -398,11 +464,11 @@ __host__ __device__ inline int down_wave_lds_words(int f, int R, int nt) {
 // prefetch of the next tile's codes, so waiting for them does not wait for
 // the prefetch), then run the tile.
 template <int BITS, int NT>
-__device__ __forceinline__ void down_item(const LayerArgs &a, const WorkItem &it, const WTile<BITS> &wt, int R,
-                                          int row0, uint32_t *wdig, float res[CHUNK_TOK], WTile<BITS> &next,
+__device__ __forceinline__ void down_item(const LayerArgs &a, const WorkItem &it, const UTile<BITS> &wt, int R,
+                                          int row0, uint32_t *wdig, float res[CHUNK_TOK], UTile<BITS> &next,
                                           bool do_next, int next_expert) {
     const int d = a.d, f = a.f, units = f / 32;
-    const int S = 64 / R, ups = ((f / 128) / S) * 4;
+    const int S = 64 / R, upl = units / S;
     const int dstride = units * XPLANES * 4 + S * 4;
     int *wsum = (int *)(wdig + NT * dstride);
     float *wscl = (float *)(wsum + NT * units);
@@ -410,23 +476,24 @@ __device__ __forceinline__ void down_item(const LayerArgs &a, const WorkItem &it
     st.load(a, it.slot0);
     if (do_next)
         next.load(a.codes + ((size_t)next_expert * 3 + 2) * ((size_t)d * f * BITS / 8),
-                  a.scales + ((size_t)next_expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R);
-    st.store(a, ups, dstride, wdig, wsum, wscl);
+                  a.scales + ((size_t)next_expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
+    st.store(a, upl, dstride, wdig, wsum, wscl);
     float r[NT];
-    tile_compute<BITS, NT>(wt, f, R, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, r);
+    utile_compute<BITS, NT>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, nullptr, r);
 #pragma unroll
     for (int j = 0; j < NT; ++j) res[j] = r[j];
 }
 
-// T <= 8: block = 4 waves on rows [row0, row0+R) of Wd for every work item;
-// wave w runs items w, w+4, ... (the next item's codes are loaded while the
-// current one computes), expert outputs land in LDS, then the block forms
-// out[t] = y_shared[t] + sum_{r asc, resident} gate[t][r] * y[slot(t, r)] and
-// x_next = x + out for those rows.
+// T <= 8: block = NW waves on rows [row0, row0+R) of Wd for every work item;
+// wave w runs items w, w+NW, ... (the next item's codes are loaded while the
+// current one computes; with NW >= the number of items every wave has at
+// most one, so all codes are requested at once), expert outputs land in
+// LDS, then the block forms out[t] = y_shared[t] + sum_{r asc, resident}
+// gate[t][r] * y[slot(t, r)] and x_next = x + out for those rows.
 template <int BITS, int NTMAX>
 __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R) {
     extern __shared__ uint32_t lds[];
-    const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
+    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, NW = blockDim.x >> 6;
     const int d = a.d, f = a.f, T = a.T, k = a.k;
     const int row0 = blockIdx.x * R;
     const int nslots = T * k + T;
@@ -436,17 +503,17 @@ __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R)
     const size_t mat_bytes = (size_t)d * f * BITS / 8;
     const size_t mat_blocks = (size_t)d * f / 256;
     // two register tiles used alternately (named, so no dynamic register
-    // indexing); item `item` computes from one while item + 4's codes load into the other
-    WTile<BITS> buf0, buf1;
+    // indexing); item `item` computes from one while item + NW's codes load into the other
+    UTile<BITS> buf0, buf1;
     WorkItem cur = a.items[min(wave, n - 1)];
     if (wave < n)
         buf0.load(a.codes + ((size_t)cur.expert * 3 + 2) * mat_bytes,
-                  a.scales + ((size_t)cur.expert * 3 + 2) * mat_blocks, f, row0, R);
-    for (int item = wave; item < n; item += 8) {
+                  a.scales + ((size_t)cur.expert * 3 + 2) * mat_blocks, f, row0, R, (f / 32) / (64 / R));
+    for (int item = wave; item < n; item += 2 * NW) {
         {
             const WorkItem it = cur;
-            const bool has = item + 4 < n;
-            if (has) cur = a.items[item + 4];
+            const bool has = item + NW < n;
+            if (has) cur = a.items[item + NW];
             float res[CHUNK_TOK];
 #define DN(nn) down_item<BITS, nn>(a, it, buf0, R, row0, wdig, res, buf1, has, cur.expert)
             NT_SWITCH(DN)
@@ -454,10 +521,10 @@ __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R)
             if (lane < R)
                 for (int j = 0; j < it.ntok; ++j) ybuf[(it.slot0 + j) * R + lane] = res[j];
         }
-        if (item + 4 < n) {
+        if (item + NW < n) {
             const WorkItem it = cur;
-            const bool has = item + 8 < n;
-            if (has) cur = a.items[item + 8];
+            const bool has = item + 2 * NW < n;
+            if (has) cur = a.items[item + 2 * NW];
             float res[CHUNK_TOK];
 #define DN(nn) down_item<BITS, nn>(a, it, buf1, R, row0, wdig, res, buf0, has, cur.expert)
             NT_SWITCH(DN)
@@ -467,7 +534,7 @@ __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R)
         }
     }
     __syncthreads();
-    for (int q = th; q < T * R; q += 256) {
+    for (int q = th; q < T * R; q += blockDim.x) {
         const int t = q / R, i = q % R;
         float s = ybuf[(T * k + t) * R + i];
         for (int r = 0; r < k; ++r) {
@@ -475,6 +542,103 @@ __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R)
             if (is_resident(a.mask, e)) s = fmaf(a.gate[t * k + r], ybuf[a.pos[t * k + r] * R + i], s);
         }
         const size_t o = (size_t)t * d + row0 + i;
+        a.out[o] = s;
+        if (a.x_next) {
+            const float xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+            a.x_next[o] = xv + s;
+        }
+    }
+}
+
+// One token: block = one wave per work item on rows [row0, row0+R) of Wd
+// (R = 64/S, S lane slices of upl units, so every expert's rows of this
+// tile are requested at once).  With no resident mask item w is slot w (the
+// shared expert slot k), so the h digit planes are staged by direct loads
+// before the work list is read; the combine inputs load meanwhile too.
+// Then out = y_shared + sum_{r asc, resident} gate[r] * y[slot(r)] and
+// x_next = x + out for those rows.
+__host__ __device__ inline int down_one_lds_words(int k, int f, int R) {
+    const int S = 64 / R, units = f / 32;
+    return (k + 1) * R + (k + 1) * (units * XPLANES * 4 + S * 4 + 2 * units) + 3 * k;
+}
+
+__device__ __forceinline__ void down_one_stage(const LayerArgs &a, int slot, uint32_t *wdig, int S, int upl) {
+    const int lane = threadIdx.x & 63, units = a.f / 32, chunks = upl * XPLANES;
+    for (int sl = 0; sl < S; ++sl) {
+        const int c = lane;
+        const uint32_t *src = a.hq + ((size_t)slot * units + sl * upl) * XPLANES * 4 + 4 * min(c, chunks - 1);
+        uint32_t *dst = wdig + dig_off(sl * upl, upl);
+        if (c < chunks) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, int R) {
+    extern __shared__ uint32_t lds[];
+    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, NW = blockDim.x >> 6;
+    const int d = a.d, f = a.f, k = a.k;
+    const int row0 = blockIdx.x * R;
+    const int S = 64 / R, units = f / 32, upl = units / S;
+    const int dstride = units * XPLANES * 4 + S * 4;
+    float *ybuf = (float *)lds;  // [k + 1][R], by slot
+    uint32_t *wdig = lds + (k + 1) * R + wave * (dstride + 2 * units);
+    int *wsum = (int *)(wdig + dstride);
+    float *wscl = (float *)(wsum + units);
+    float *cg = (float *)(lds + (k + 1) * R + NW * (dstride + 2 * units));  // [k] gate of pick r
+    int *cp = (int *)(cg + k);                                               // [k] slot of pick r
+    int *con = cp + k;                                                       // [k] resident
+    const bool fast = a.mask == nullptr;
+    int slot = wave < k ? wave : k;
+    if (fast) down_one_stage(a, slot, wdig, S, upl);
+    int sv = 0;
+    float cv = 0.f;
+    if (fast && lane < units) {
+        sv = a.hsum[(size_t)slot * units + lane];
+        cv = a.hscl[(size_t)slot * units + lane];
+    }
+    int pe = 0, pp = 0;
+    float pg = 0.f;
+    if (wave == 0 && lane < k) {
+        pe = a.idx[lane];
+        pg = a.gate[lane];
+        pp = a.pos[lane];
+    }
+    const int n = *a.n_items;
+    if (wave < n) {
+        const WorkItem it = a.items[wave];
+        if (!fast) {
+            slot = it.slot0;
+            down_one_stage(a, slot, wdig, S, upl);
+            if (lane < units) {
+                sv = a.hsum[(size_t)slot * units + lane];
+                cv = a.hscl[(size_t)slot * units + lane];
+            }
+        }
+        UTile<BITS> wt;
+        wt.load(a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
+                a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
+        if (lane < units) {
+            wsum[lane] = sv;
+            wscl[lane] = cv;
+        }
+        // this wave's staged planes have landed and its LDS writes precede its reads
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        float res[1];
+        utile_compute<BITS, 1>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, nullptr, res);
+        if (lane < R) ybuf[slot * R + lane] = res[0];
+    }
+    if (wave == 0 && lane < k) {
+        cg[lane] = pg;
+        cp[lane] = pp;
+        con[lane] = is_resident(a.mask, pe) ? 1 : 0;
+    }
+    __syncthreads();
+    for (int i = th; i < R; i += blockDim.x) {
+        float s = ybuf[k * R + i];
+        for (int r = 0; r < k; ++r)
+            if (con[r]) s = fmaf(cg[r], ybuf[cp[r] * R + i], s);
+        const size_t o = (size_t)row0 + i;
         a.out[o] = s;
         if (a.x_next) {
             const float xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
@@ -494,9 +658,9 @@ __global__ __launch_bounds__(128) void gemv_down_items_kernel(LayerArgs a, int R
     if (item >= *a.n_items) return;
     const WorkItem it = a.items[item];
     const int row0 = ((blockIdx.x % wg_per_item) * 2 + wave) * R;
-    WTile<BITS> wt;
+    UTile<BITS> wt;
     wt.load(a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
-            a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R);
+            a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, (f / 32) / (64 / R));
     uint32_t *wdig = lds + wave * down_wave_lds_words(f, R, NTMAX);
     float res[CHUNK_TOK];
 #define DN(nn) down_item<BITS, nn>(a, it, wt, R, row0, wdig, res, wt, false, 0)
@@ -507,23 +671,11 @@ __global__ __launch_bounds__(128) void gemv_down_items_kernel(LayerArgs a, int R
 }
 
 // ------------------------------------------------------------- launchers
-// Column slices per wave for an input width `in`: the most slices (up to 4)
-// that split the 128-column groups evenly with at most MAXQ per slice.
-static inline int pick_slices(int in) {
-    const int Q = in / 128;
-    for (int S = 4; S >= 1; S >>= 1)
-        if (Q % S == 0 && Q / S <= MAXQ) return S;
-    return 0;
-}
-
 inline bool gemv_supported_impl(int d, int f, int bits) {
     if (bits != 3 && bits != 2) return false;
+    if (unit_slices(d, 8) < 2 || unit_slices(f, 8) < 1) return false;   // decode tiles
     if (d % 128 || f % 128 || f > 32 * MAX_HUNITS || d > 8192) return false;
-    const int Sg = pick_slices(d), Sd = pick_slices(f);
-    if (!Sg || !Sd) return false;
-    const int Rg = 64 / Sg, Rd = 64 / Sd;
-    if (Rg > 32) return false;             // one wave forms h of 8 tokens x 2R columns
-    if (f % (2 * Rg)) return false;        // gate/up blocks own 2R rows of f
+    const int Rd = 64 / unit_slices(f, 8);
     if (d % (2 * Rd)) return false;        // down blocks own R (rows kernel) or 2R rows
     return true;
 }
@@ -549,17 +701,17 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
     } while (0)
 
 template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / pick_slices(a.d);
+    const int R = 64 / unit_slices(a.d, 8);
     const int nt = nt_round(ntmax_for(a.T));
-    const int off = gateup_lds_words(a.d, R, nt);
+    const int off = gateup_lds_words(a.d, R, a.T, nt);
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
-    const dim3 grid(max_items * (a.f / (2 * R)) + 1);
-    LAUNCH_NT(gemv_gateup_small_kernel, BITS, nt, grid, 256, lds, s, a, R, off);
+    const dim3 grid(max_items * (a.f / 32) + 1);
+    LAUNCH_NT(gemv_gateup_small_kernel, BITS, nt, grid, 64 * 2 * (32 / R), lds, s, a, R, off);
     return hipGetLastError();
 }
 
 template <int BITS> hipError_t down_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / pick_slices(a.f);
+    const int R = 64 / unit_slices(a.f, 8);
     const int nt = nt_round(ntmax_for(a.T));
     const size_t lds = 4 * (size_t)2 * down_wave_lds_words(a.f, R, nt);
     const dim3 grid(max_items * (a.d / (2 * R)));
@@ -567,17 +719,31 @@ template <int BITS> hipError_t down_launch(const LayerArgs &a, int max_items, hi
     return hipGetLastError();
 }
 
-static inline size_t down_rows_lds(int T, int k, int f, int R, int nt) {
+// Waves of the down rows kernels: one token, one per work item (k + 1);
+// else 4, or fewer when the LDS does not hold them.
+static inline size_t down_rows_lds(int T, int k, int f, int R, int nt, int nw) {
     const int nslots = T * k + T;
-    return 4 * ((size_t)nslots * R + 4 * (size_t)down_wave_lds_words(f, R, nt));
+    return 4 * ((size_t)nslots * R + (size_t)nw * down_wave_lds_words(f, R, nt));
+}
+static inline int down_rows_waves(int T, int k, int f, int R, int nt) {
+    int nw = T == 1 ? k + 1 : 4;
+    while (nw > 1 && down_rows_lds(T, k, f, R, nt, nw) > LDS_LIMIT) --nw;
+    return nw;
 }
 
 template <int BITS> hipError_t down_rows_launch(const LayerArgs &a, hipStream_t s) {
-    const int R = 64 / pick_slices(a.f);
+    const int R = 64 / unit_slices(a.f, 8);
     const int nt = nt_round(ntmax_for(a.T));
-    const size_t lds = down_rows_lds(a.T, a.k, a.f, R, nt);
+    const int nw = down_rows_waves(a.T, a.k, a.f, R, nt);
+    const size_t lds = down_rows_lds(a.T, a.k, a.f, R, nt, nw);
     const dim3 grid(a.d / R);
-    LAUNCH_NT(gemv_down_rows_kernel, BITS, nt, grid, 256, lds, s, a, R);
+    if (a.T == 1) {
+        const size_t lds1 = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
+        if (lds1 > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(gemv_down_rows_one_kernel<BITS>, grid, dim3(64 * (a.k + 1)), lds1, s, a, R);
+        return hipGetLastError();
+    }
+    LAUNCH_NT(gemv_down_rows_kernel, BITS, nt, grid, 64 * nw, lds, s, a, R);
     return hipGetLastError();
 }
 

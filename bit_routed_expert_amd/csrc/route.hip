@@ -7,6 +7,8 @@
 // Qwen3.8-Flash-Next？", section 一); the GPU runs the router (same page,
 // section 二).  Logits are fp32; top-k is ordered by (logit desc, index asc);
 // gates are the softmax renormalised over the k picks.
+#include <algorithm>
+
 #include "routing.hpp"
 #include "mfma.hpp"
 
@@ -88,7 +90,7 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
 // before anything else, dotted with the T token rows staged in LDS; the
 // unnormalised logits go to z.  Blocks past those: one per token, its
 // inverse RMS and (unless routing only) its input digit planes.  The top-k
-// is taken later by every consumer block from z (a few KB), so no block
+// is taken afterwards by every consumer block from z (a few KB), so no block
 // waits on another inside this kernel.
 constexpr int RS_WAVES = 4;   // router rows per block
 constexpr int RS_MAXJ = 8;    // float4 per lane per 2048-column chunk
@@ -109,6 +111,9 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
     const int e = blockIdx.x * RS_WAVES + wave;
     const float *wrow = a.Wr + (size_t)(e < E ? e : 0) * d;
     float *xs = lds;  // [T][d]
+    float zacc[CHUNK_TOK];
+#pragma unroll
+    for (int t = 0; t < CHUNK_TOK; ++t) zacc[t] = 0.f;
     for (int c0 = 0; c0 < d; c0 += 64 * 4 * RS_MAXJ) {
         float4 wv[RS_MAXJ];
 #pragma unroll
@@ -121,22 +126,26 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
                 xs[i] = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
             __syncthreads();
         }
-        for (int t = 0; t < T; ++t) {
-            float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < RS_MAXJ; ++j) {
-                const int i = c0 + lane * 4 + 256 * j;
-                if (i < d) {
-                    const float4 xv = *(const float4 *)(xs + t * d + i);
-                    acc += wv[j].x * xv.x + wv[j].y * xv.y + wv[j].z * xv.z + wv[j].w * xv.w;
+        for (int t = 0; t < CHUNK_TOK; ++t) {
+            if (t < T) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < RS_MAXJ; ++j) {
+                    const int i = c0 + lane * 4 + 256 * j;
+                    if (i < d) {
+                        const float4 xv = *(const float4 *)(xs + t * d + i);
+                        acc += wv[j].x * xv.x + wv[j].y * xv.y + wv[j].z * xv.z + wv[j].w * xv.w;
+                    }
                 }
-            }
-            acc = wave_sum(acc);
-            if (lane == 0 && e < E) {
-                if (c0 == 0) a.z[t * E + e] = acc;
-                else a.z[t * E + e] += acc;
+                zacc[t] += wave_sum(acc);
             }
         }
+    }
+    if (lane == 0 && e < E) {
+#pragma unroll
+        for (int t = 0; t < CHUNK_TOK; ++t)
+            if (t < T) a.z[t * E + e] = zacc[t];
     }
 }
 
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
 __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
     extern __shared__ uint32_t lds_u[];
     const SmallRoute L(lds_u, a.E);
-    small_route_compute(a, L);
+    small_route_compute(a, L, a.z, a.inv_rms);
     small_route_write(a, L);
 }
 

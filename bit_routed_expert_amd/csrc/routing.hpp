@@ -16,42 +16,31 @@ __device__ __forceinline__ uint32_t f32_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// DPP lane swap within rows of 16 (quad perms and row mirrors).
-template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-// Maximum of a 64-bit key over the wave, returned uniform: the 16-lane rows
-// reduce through DPP lane swaps, the four row maxima through readlane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = u64_max(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = u64_max(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = u64_max(v, dpp64<0x141>(v));  // row_half_mirror
-    v = u64_max(v, dpp64<0x140>(v));  // row_mirror
-    uint64_t m = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
-        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
-        m = u64_max(m, ((uint64_t)hi << 32) | lo);
+// Maximum / minimum of a 32-bit value over the wave (uniform result).
+template <bool MAX> __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+#define RED_STEP(CTRL)                                                                         \
+    {                                                                                          \
+        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false); \
+        v = MAX ? (v > o ? v : o) : (v < o ? v : o);                                           \
     }
-    return m;
+    RED_STEP(0xB1) RED_STEP(0x4E) RED_STEP(0x141) RED_STEP(0x140)
+#undef RED_STEP
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    const uint32_t a = MAX ? (r0 > r1 ? r0 : r1) : (r0 < r1 ? r0 : r1);
+    const uint32_t b = MAX ? (r2 > r3 ? r2 : r3) : (r2 < r3 ? r2 : r3);
+    return MAX ? (a > b ? a : b) : (a < b ? a : b);
 }
 
 // Ordered top-k of E logits z[e] * scale + bias[e] by one wave (JM = E/64
-// rounded up to 8 or 16).  Each lane sorts its JM candidates once by the
-// composite key (value, ~index); every round takes the wave maximum of the
-// lanes' heads and the lane owning it pops its head.  Lane r < k ends with
-// pick r: *e_out, *z_out.
+// rounded up to 8 or 16); lane r < k ends with pick r: *e_out, *z_out.  Each lane sorts its JM candidates by
+// (value desc, index asc); a round takes the wave maximum of the lanes'
+// head values (32-bit) and, only when several lanes hold that value, the
+// smallest of their head indices; the owning lane pops its head.
 template <int JM>
-__device__ __forceinline__ void wave_topk_picks(const float *z, int E, int k, float scale, const float *bias,
-                                                int *e_out, float *z_out) {
+__device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
+                                                     int *e_out, float *z_out) {
     const int lane = threadIdx.x & 63;
-    // all loads first, from clamped addresses, so they are in flight together
     float zv[JM], bv[JM];
 #pragma unroll
     for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
@@ -61,14 +50,14 @@ __device__ __forceinline__ void wave_topk_picks(const float *z, int E, int k, fl
 #pragma unroll
         for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
     }
-    uint64_t key[JM];
+    uint32_t kv[JM], ki[JM];   // value key (0 = empty), expert index
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
         const int e = lane + 64 * j;
-        const float v = zv[j] * scale + bv[j];
-        key[j] = (e < E) ? (((uint64_t)f32_key(v) << 32) | (uint32_t)(~(uint32_t)e)) : 0;
+        kv[j] = (e < E) ? f32_key(zv[j] * scale + bv[j]) : 0u;
+        ki[j] = (uint32_t)e;
     }
-    // bitonic sort, descending
+    // bitonic sort, descending by (kv, -ki); indices of one lane increase with j
 #pragma unroll
     for (int kk = 2; kk <= JM; kk <<= 1)
 #pragma unroll
@@ -78,31 +67,150 @@ __device__ __forceinline__ void wave_topk_picks(const float *z, int E, int k, fl
                 const int l = i ^ jj;
                 if (l > i) {
                     const bool desc = (i & kk) == 0;
-                    const uint64_t a = key[i], b = key[l];
-                    const bool sw = desc ? (a < b) : (a > b);
-                    key[i] = sw ? b : a;
-                    key[l] = sw ? a : b;
+                    const bool a_first = kv[i] > kv[l] || (kv[i] == kv[l] && ki[i] < ki[l]);
+                    const bool sw = desc ? !a_first : a_first;
+                    const uint32_t tv = kv[i], ti = ki[i];
+                    kv[i] = sw ? kv[l] : tv;
+                    ki[i] = sw ? ki[l] : ti;
+                    kv[l] = sw ? tv : kv[l];
+                    ki[l] = sw ? ti : ki[l];
                 }
             }
     int my_e = 0;
-    float my_z = 0.f;
+    uint32_t my_k = 0x80000000u;   // key of 0.0 for lanes past k
     for (int r = 0; r < k; ++r) {
-        const uint64_t m = wave_max_u64(key[0]);
-        const uint32_t kh = (uint32_t)(m >> 32);
-        const int e = (int)(~(uint32_t)m);
-        const uint32_t u = (kh & 0x80000000u) ? (kh & 0x7FFFFFFFu) : ~kh;
-        if (lane == r) {
-            my_e = e;
-            my_z = __uint_as_float(u);
+        const uint32_t m = wave_reduce_u32<true>(kv[0]);
+        const uint64_t ball = __ballot(kv[0] == m);
+        uint32_t e;
+        if (__popcll(ball) == 1) {
+            e = (uint32_t)__builtin_amdgcn_readlane((int)ki[0], __ffsll((unsigned long long)ball) - 1);
+        } else {
+            e = wave_reduce_u32<false>(kv[0] == m ? ki[0] : 0xFFFFFFFFu);
         }
-        if (key[0] == m) {  // the owner pops its head
+        if (lane == r) {
+            my_e = (int)e;
+            my_k = m;
+        }
+        if (kv[0] == m && ki[0] == e) {  // the owner pops its head
 #pragma unroll
-            for (int j = 0; j < JM - 1; ++j) key[j] = key[j + 1];
-            key[JM - 1] = 0;
+            for (int j = 0; j < JM - 1; ++j) {
+                kv[j] = kv[j + 1];
+                ki[j] = ki[j + 1];
+            }
+            kv[JM - 1] = 0u;
         }
     }
     *e_out = my_e;
-    *z_out = my_z;
+    *z_out = __uint_as_float((my_k & 0x80000000u) ? (my_k & 0x7FFFFFFFu) : ~my_k);
+}
+
+// Ordered top-k by threshold: tau = the k-th largest value key (bitwise
+// search, each step counting keys >= candidate with one ballot per
+// candidate slot), the picks are the keys above tau plus the lowest-index
+// keys equal to tau, and each pick's place in (value desc, index asc) order
+// is its rank among the picks.  Same contract as wave_topk_picks_fast; with
+// sel[j] (optional) = the 64-bit ballot of picked experts 64j .. 64j+63.
+template <int JM>
+__device__ __forceinline__ void wave_topk_picks_tau(const float *z, int E, int k, float scale, const float *bias,
+                                                    int *e_out, float *z_out, uint64_t *sel) {
+    const int lane = threadIdx.x & 63;
+    float zv[JM], bv[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) bv[j] = 0.f;
+    if (bias) {
+#pragma unroll
+        for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+    }
+    uint32_t kv[JM];   // value keys, 0 for slots past E (below every real key)
+#pragma unroll
+    for (int j = 0; j < JM; ++j) kv[j] = (lane + 64 * j < E) ? f32_key(zv[j] * scale + bv[j]) : 0u;
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) cnt += __popcll(__ballot(kv[j] >= cand));
+        if (cnt >= k) tau = cand;
+    }
+    // picks: keys above tau, then ties at tau in index order (j asc, lane asc)
+    uint64_t pick[JM];
+    int rem = k;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        pick[j] = __ballot(kv[j] > tau);
+        rem -= __popcll(pick[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        uint64_t eq = __ballot(kv[j] == tau);
+        while (rem > 0 && eq) {
+            const uint64_t low = eq & (~eq + 1ull);
+            pick[j] |= low;
+            eq ^= low;
+            --rem;
+        }
+    }
+    if (sel) {
+#pragma unroll
+        for (int j = 0; j < JM; ++j) sel[j] = pick[j];
+    }
+    // pick r (in index order) -> lane r; its rank by (value desc, index asc)
+    int my_e = 0, pe = -1;
+    uint32_t pk = 0;
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const bool mine = (pick[j] >> lane) & 1ull;
+        const int before = r + __popcll(pick[j] & ((1ull << lane) - 1ull));
+        // lane `before` receives this pick: gather via LDS-free shuffles below
+        if (mine) { pe = before; }
+        r += __popcll(pick[j]);
+        (void)my_e;
+    }
+    // move (e, key) of every pick to lane `rank-in-index-order` with ds_bpermute-free loops
+    int ie = 0;
+    uint32_t ik = 0;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        uint64_t m = pick[j];
+        int base = 0;
+#pragma unroll
+        for (int jj = 0; jj < JM; ++jj) base += jj < j ? __popcll(pick[jj]) : 0;
+        while (m) {
+            const int src = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1ull;
+            const uint32_t kk = (uint32_t)__builtin_amdgcn_readlane((int)kv[j], src);
+            if (lane == base) {
+                ie = src + 64 * j;
+                ik = kk;
+            }
+            ++base;
+        }
+    }
+    (void)pe;
+    // rank of the pick held by lane r < k
+    int rank = 0;
+    for (int q = 0; q < k; ++q) {
+        const uint32_t qk = (uint32_t)__shfl((int)ik, q, WAVE);
+        const int qe = __shfl(ie, q, WAVE);
+        rank += (qk > ik || (qk == ik && qe < ie)) ? 1 : 0;
+    }
+    // lane `rank` takes the pick
+    int oe = 0;
+    uint32_t ok = 0x80000000u;
+    for (int q = 0; q < k; ++q) {
+        const int qr = __shfl(rank, q, WAVE);
+        const int qe = __shfl(ie, q, WAVE);
+        const uint32_t qk = (uint32_t)__shfl((int)ik, q, WAVE);
+        if (lane == qr) {
+            oe = qe;
+            ok = qk;
+        }
+    }
+    *e_out = oe;
+    *z_out = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
 }
 
 // Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
@@ -113,9 +221,9 @@ __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float sc
     int e;
     float v;
     if (E <= 512)
-        wave_topk_picks<8>(z, E, k, scale, bias, &e, &v);
+        wave_topk_picks_fast<8>(z, E, k, scale, bias, &e, &v);
     else
-        wave_topk_picks<16>(z, E, k, scale, bias, &e, &v);
+        wave_topk_picks_fast<16>(z, E, k, scale, bias, &e, &v);
     const float top = __shfl(v, 0, WAVE);
     const float p = (lane < k) ? expf(v - top) : 0.f;
     const float s = wave_sum(p);
@@ -175,16 +283,17 @@ struct SmallRoute {
           tmp((int32_t *)(base + E + 32 + 512)) {}
 };
 
-// Every block: top-k of its T <= 8 tokens (one wave per token) from the
-// unnormalised logits z and the tokens' inverse RMS, then per-expert token
-// masks and the bitmap of picked resident experts.
-__device__ __forceinline__ void small_route_compute(const LayerArgs &a, const SmallRoute &L) {
+// Top-k of T <= 8 tokens (one wave per token) from the unnormalised logits
+// z[t][E] and the tokens' inverse RMS inv[t] (both may sit in LDS), then
+// per-expert token masks and the bitmap of picked resident experts.
+__device__ __forceinline__ void small_route_compute(const LayerArgs &a, const SmallRoute &L, const float *z,
+                                                    const float *inv) {
     const int th = threadIdx.x, wave = th >> 6, nw = blockDim.x >> 6;
     const int E = a.E, k = a.k, T = a.T;
     for (int i = th; i < E; i += blockDim.x) L.tokmask[i] = 0;
     if (th < 32) L.picked[th] = 0;
     for (int t = wave; t < T; t += nw)
-        wave_topk(a.z + t * E, E, k, a.inv_rms[t], a.bias, nullptr, nullptr, nullptr, nullptr, L.sidx + t * k,
+        wave_topk(z + t * E, E, k, inv[t], a.bias, nullptr, nullptr, nullptr, nullptr, L.sidx + t * k,
                   L.sgate + t * k);
     __syncthreads();
     if (th < T * k) {
@@ -195,43 +304,46 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
     __syncthreads();
 }
 
-// Work item `item` of this routing: the item-th picked resident expert in
-// ascending order, or, for item == (number of them), the shared expert with
-// all T tokens.  Slots of expert e start at the number of picks of experts
-// below e.  Returns false past the last item.  toks[j] = token of slot j.
+// Work item `item` of this routing, computed by every wave alike (no block
+// barrier): the item-th picked resident expert in ascending order, or, for
+// item == their number, the shared expert with all T tokens.  Slots of
+// expert e start at the number of picks of experts below e.  Returns false
+// past the last item.  toks[j] = token of slot j.
 __device__ __forceinline__ bool small_route_item(const LayerArgs &a, const SmallRoute &L, int item, WorkItem &it,
                                                  int *toks) {
-    const int th = threadIdx.x, n = a.T * a.k;
-    int nres = 0;
-    for (int w = 0; w < 32; ++w) nres += __popc(L.picked[w]);
+    const int lane = threadIdx.x & 63, n = a.T * a.k;
+    const int c = lane < 32 ? __popc(L.picked[lane]) : 0;
+    int pre = c;   // inclusive prefix of the bitmap word counts
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        const int t = __shfl_up(pre, o, WAVE);
+        if (lane >= o) pre += t;
+    }
+    const int nres = __shfl(pre, 31, WAVE);
     if (item > nres) return false;
     if (item == nres) {
         it = WorkItem{a.E, n, a.T};
-        for (int j = 0; j < a.T; ++j) toks[j] = j;
+#pragma unroll
+        for (int j = 0; j < CHUNK_TOK; ++j) toks[j] = j;
         return true;
     }
-    if (th < n) {
-        const int e = L.sidx[th], t = th / a.k;
-        const uint32_t mk = (uint32_t)L.tokmask[e];
-        if (is_resident(a.mask, e) && (int)__ffs(mk) - 1 == t) {  // first pick of e
-            int rank = 0;
-            for (int w = 0; w < (e >> 5); ++w) rank += __popc(L.picked[w]);
-            rank += __popc(L.picked[e >> 5] & ((1u << (e & 31)) - 1u));
-            if (rank == item) {
-                int below = 0;
-                for (int j = 0; j < n; ++j) below += L.sidx[j] < e ? 1 : 0;
-                L.tmp[8] = e;
-                L.tmp[9] = below;
-            }
-        }
+    const int w = __ffsll((unsigned long long)__ballot(lane < 32 && pre > item)) - 1;
+    uint32_t word = L.picked[w];
+    for (int r = item - (__shfl(pre, w, WAVE) - __shfl(c, w, WAVE)); r > 0; --r) word &= word - 1u;
+    const int e = w * 32 + __ffs(word) - 1;
+    int below = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        below += __popcll(__ballot(j < n && L.sidx[min(j, n - 1)] < e));
     }
-    __syncthreads();
-    const int e = L.tmp[8];
     const uint32_t mk = (uint32_t)L.tokmask[e];
-    it = WorkItem{e, L.tmp[9], (int32_t)__popc(mk)};
-    int j = 0;
-    for (int t = 0; t < a.T; ++t)
-        if ((mk >> t) & 1u) toks[j++] = t;
+    it = WorkItem{e, below, (int32_t)__popc(mk)};
+    uint32_t rest = mk;   // toks[j]: the j-th set bit (fixed indices keep toks in registers)
+#pragma unroll
+    for (int j = 0; j < CHUNK_TOK; ++j) {
+        toks[j] = rest ? __ffs(rest) - 1 : 0;
+        rest &= rest - 1u;
+    }
     return true;
 }
 
