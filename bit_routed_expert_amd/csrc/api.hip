@@ -19,8 +19,8 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr int SMALL_T = 8;
 
 struct Layout {
-    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hq, hsum,
-        hscl, xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
+    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf, xa, sx,
+        ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -59,9 +59,7 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.xq = take((size_t)Tq * (d / 32) * XPLANES * 16);
     l.xsum = take(4 * Tq * (d / 32));
     l.xscl = take(4 * Tq * ((d + 255) / 256));
-    l.hq = take((size_t)Sq * (f / 32) * XPLANES * 16);
-    l.hsum = take(4 * Sq * (f / 32));
-    l.hscl = take(4 * Sq * (f / 32));
+    l.hf = take(4 * Sq * f);
     l.xa = take((size_t)2 * Tg * d * 2);
     l.sx = take(4 * Tg * (d / 128));
     l.ha = take((size_t)2 * Sg * f * 2);
@@ -111,9 +109,7 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xq = (uint32_t *)(ws + l.xq);
     a.xsum = (int32_t *)(ws + l.xsum);
     a.xscl = (float *)(ws + l.xscl);
-    a.hq = (uint32_t *)(ws + l.hq);
-    a.hsum = (int32_t *)(ws + l.hsum);
-    a.hscl = (float *)(ws + l.hscl);
+    a.hf = (float *)(ws + l.hf);
     a.Y = (float *)(ws + l.Y);
     a.xa = (uint16_t *)(ws + l.xa);
     a.sx = (float *)(ws + l.sx);
@@ -138,10 +134,10 @@ struct Recorder {
     int n, i;
     hipStream_t s;
     void before() {
-        if (events && i < n) hipEventRecord((hipEvent_t)events[2 * i], s);
+        if (events && i < n) (void)hipEventRecord((hipEvent_t)events[2 * i], s);
     }
     void after() {
-        if (events && i < n) hipEventRecord((hipEvent_t)events[2 * i + 1], s);
+        if (events && i < n) (void)hipEventRecord((hipEvent_t)events[2 * i + 1], s);
         ++i;
     }
 };

@@ -135,11 +135,7 @@ struct LayerArgs {
     uint32_t *xq;
     int32_t *xsum;
     float *xscl;
-    // SwiGLU activation h of each slot, quantised per 32-column unit:
-    // [slots][f/32][XPLANES][4] words, per-unit digit sums and 2^-E
-    uint32_t *hq;
-    int32_t *hsum;
-    float *hscl;
+    float *hf;           // [slots][f] SwiGLU activation h of each slot (decode path)
     float *Y;            // [slots][d] expert outputs (larger T)
     // GEMM path: bf16 hi/lo activations, columns permuted inside each
     // 128-column step, and their sums over each step (x) or 32-feature group (h)

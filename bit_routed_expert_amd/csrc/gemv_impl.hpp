@@ -255,7 +255,7 @@ struct GuLds {
 __host__ __device__ inline int gateup_lds_words(int d, int R, int T, int nt) {
     const int S = 64 / R;
     const int dstride = (d / 32) * XPLANES * 4 + S * 4;
-    return T * dstride + T * (d / 32) + T * ((d + 255) / 256) + 2 * nt * 32;
+    return T * dstride + T * (d / 32) + T * ((d + 255) / 256) + nt * 4 * R;
 }
 
 // Staging of every token's input digit planes into LDS by direct
@@ -276,18 +276,16 @@ __device__ __forceinline__ void xstage_issue(const LayerArgs &a, const GuLds &g,
         if (c < chunks) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
 }
-// Gate/up for the NT tokens toks[] of one work item: waves [0, NWM) take
-// gate rows j0 + R*w .. +R, waves [NWM, 2*NWM) the same rows of up (NWM =
-// 32 / R, so a block owns 32 columns of h).  Then h = silu(g) * u for those
-// 32 columns, quantised per 32 columns, goes to hq/hsum/hscl.
+// Gate/up for the NT tokens toks[] of one work item: waves [0, G) take gate
+// rows j0 + R*w .. +R, waves [G, 2G) the same rows of up; then h = silu(g)
+// * u (fp32) of those G*R columns goes to hf.
 template <int BITS, int NT>
 __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &it, const int *toks, int R,
                                             int j0, const GuLds &g) {
-    const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
-    const int d = a.d, f = a.f, NWM = 32 / R;
-    const int m = wave / NWM;  // 0 gate, 1 up
-    const int row0 = j0 + (wave % NWM) * R;
+    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, G = blockDim.x >> 7;
+    const int d = a.d, f = a.f;
     const int upl = (d / 32) / (64 / R);
+    const int m = wave / G, row0 = j0 + (wave % G) * R;
     const size_t mat_bytes = (size_t)d * f * BITS / 8;
     const size_t mat_blocks = (size_t)d * f / 256;
     const size_t mi = (size_t)it.expert * 3 + m;
@@ -298,43 +296,16 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     float res[NT];
     utile_compute<BITS, NT>(wt, R, upl, unit_period(d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl, g.G,
                             XGROUP_UNITS, toks, res);
-    if (lane < R) {
+    if (m == 1 && lane < R) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) g.gu[(m * NT + j) * 32 + (wave % NWM) * R + lane] = res[j];
+        for (int j = 0; j < NT; ++j) g.gu[j * G * R + (wave - G) * R + lane] = res[j];
     }
     __syncthreads();
-    // h for NT tokens x 32 columns: one chunk of 8 columns per lane of wave 0
-    if (wave == 0) {
-        const int c = lane & 3, j = lane >> 2;
-        const bool valid = j < NT;
-        const int jj = valid ? j : 0;
-        float h[8];
-        float mx = 0.f;
+    if (m == 0 && lane < R) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const float gv = g.gu[jj * 32 + c * 8 + n];
-            const float u = g.gu[(NT + jj) * 32 + c * 8 + n];
-            h[n] = valid ? gv / (1.f + expf(-gv)) * u : 0.f;
-            mx = fmaxf(mx, fabsf(h[n]));
-        }
-        // a 32-column group is 4 consecutive lanes
-        mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
-        const int E = fixed_point_exponent<XPLANES>(mx);
-        uint32_t word[XPLANES];
-        int sx = chunk_digits(h, E, word);
-        sx += __shfl_xor(sx, 1, WAVE);
-        sx += __shfl_xor(sx, 2, WAVE);
-        if (valid) {
-            const int slot = it.slot0 + j;
-            const int U = j0 / 32;
-            uint32_t *dst = a.hq + ((size_t)slot * (f / 32) + U) * (XPLANES * 4);
-#pragma unroll
-            for (int p = 0; p < XPLANES; ++p) dst[p * 4 + c] = word[p];
-            if (c == 0) {
-                a.hsum[(size_t)slot * (f / 32) + U] = sx;
-                a.hscl[(size_t)slot * (f / 32) + U] = ldexpf(1.f, -E);
-            }
+        for (int j = 0; j < NT; ++j) {
+            const float gv = res[j], u = g.gu[j * G * R + wave * R + lane];
+            a.hf[(size_t)(it.slot0 + j) * f + row0 + lane] = gv / (1.f + expf(-gv)) * u;
         }
     }
 }
@@ -352,14 +323,15 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
         default: break;                                               \
     }
 
-// T <= 8: every block (2 * 32/R waves, 32 columns of h) takes the top-k of
+// T <= 8: every block (2G waves, G*R columns of h; G = 1 for one token, 4
+// otherwise so the tokens' top-k run on separate waves) takes the top-k of
 // the T tokens itself from the router logits (a few KB) while its input
 // digit planes, unit sums and group scales load, derives its own work item
 // and runs it; the last block writes the routing outputs and the work list
 // instead.
 template <int BITS, int NTMAX>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_gateup_small_kernel(
-    LayerArgs a, int R, int route_off) {
+__global__ __launch_bounds__(NTMAX == 1 ? 128 : 512) void gemv_gateup_small_kernel(LayerArgs a, int R,
+                                                                                   int route_off) {
     extern __shared__ uint32_t lds[];
     const GuLds g(lds, a.d, R, a.T, NTMAX);
     const SmallRoute L(lds + route_off, a.E);
@@ -392,60 +364,67 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         if (i < g.units) g.sum[j * g.units + i] = a.xsum[(size_t)j * g.units + i];
         else g.scl[j * g.G + i - g.units] = a.xscl[(size_t)j * g.G + i - g.units];
     }
-    const int wg_per_item = a.f / 32;
+    const int cols = (blockDim.x >> 7) * R, wg_per_item = a.f / cols;
     WorkItem it;
     int toks[CHUNK_TOK];
     if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, toks)) return;
-    const int j0 = (blockIdx.x % wg_per_item) * 32;
+    const int j0 = (blockIdx.x % wg_per_item) * cols;
 #define GU(n) gateup_body<BITS, n>(a, it, toks, R, j0, g)
     NT_SWITCH(GU)
 #undef GU
 }
 
 // ----------------------------------------------------------------- down
-// The h digit planes, unit sums and group scales of NT consecutive slots,
-// staged through registers into one wave's LDS region.  load() issues the
-// global loads; store() writes them (so a caller can issue other loads in
-// between without the in-order load counter making store() wait for them).
+// h of NT consecutive slots (fp32, [slot][f]) staged through registers and
+// quantised into one wave's LDS region: per 32-column unit, 24-bit fixed
+// point with exponent E from the unit's max |h|, 6 balanced base-16 digit
+// planes, the unit's digit sum and 2^-E.  A lane takes 8-column chunks
+// c = lane + 64u; the 4 chunks of a unit sit in 4 neighbouring lanes.
+// load() issues the global loads; store() quantises and writes (so a
+// caller can issue other loads in between without the in-order load
+// counter making store() wait for them).
 template <int NT> struct HStage {
-    static constexpr int PER = (NT * MAX_HUNITS * XPLANES + 63) / 64;  // uint4 per lane
-    static constexpr int PERS = (NT * MAX_HUNITS + 63) / 64;           // sums / scales per lane
-    uint4 v[PER];
-    int sv[PERS];
-    float cv[PERS];
+    static constexpr int PER = (NT * MAX_HUNITS * 4 + 63) / 64;   // chunks per lane
+    float4 v[PER][2];
 
     __device__ __forceinline__ void load(const LayerArgs &a, int slot0) {
-        const int lane = threadIdx.x & 63, units = a.f / 32;
-        const int n16 = NT * units * XPLANES, ns = NT * units;
-        const uint4 *src = (const uint4 *)(a.hq + (size_t)slot0 * units * XPLANES * 4);
+        const int lane = threadIdx.x & 63, nch = NT * (a.f / 8);
+        const float4 *src = (const float4 *)(a.hf + (size_t)slot0 * a.f);
 #pragma unroll
-        for (int u = 0; u < PER; ++u) v[u] = src[min(lane + 64 * u, n16 - 1)];
-#pragma unroll
-        for (int u = 0; u < PERS; ++u) {
-            const int i = min(lane + 64 * u, ns - 1);
-            sv[u] = a.hsum[(size_t)slot0 * units + i];
-            cv[u] = a.hscl[(size_t)slot0 * units + i];
+        for (int u = 0; u < PER; ++u) {
+            const int c = min(lane + 64 * u, nch - 1);
+            v[u][0] = src[2 * c];
+            v[u][1] = src[2 * c + 1];
         }
     }
 
     __device__ __forceinline__ void store(const LayerArgs &a, int ups, int dstride, uint32_t *wdig, int *wsum,
                                           float *wscl) const {
-        const int lane = threadIdx.x & 63, units = a.f / 32;
-        const int n16u = units * XPLANES, n16 = NT * n16u, ns = NT * units;
+        const int lane = threadIdx.x & 63, units = a.f / 32, cps = a.f / 8, nch = NT * cps;
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int i = lane + 64 * u;
-            if (i < n16) {
-                const int j = i / n16u, q = i % n16u, U = q / XPLANES, p = q % XPLANES;
-                *(uint4 *)(wdig + j * dstride + dig_off(U, ups) + 4 * p) = v[u];
-            }
-        }
+            const int c = lane + 64 * u;
+            const float h[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                                v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+            float mx = 0.f;
 #pragma unroll
-        for (int u = 0; u < PERS; ++u) {
-            const int i = lane + 64 * u;
-            if (i < ns) {
-                wsum[i] = sv[u];
-                wscl[i] = cv[u];
+            for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
+            mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+            const int E = fixed_point_exponent<XPLANES>(mx);
+            uint32_t word[XPLANES];
+            int sx = chunk_digits(h, E, word);
+            sx += __shfl_xor(sx, 1, WAVE);
+            sx += __shfl_xor(sx, 2, WAVE);
+            if (c < nch) {
+                const int j = c / cps, cc = c % cps, U = cc / 4, q = cc % 4;
+                uint32_t *dst = wdig + j * dstride + dig_off(U, ups);
+#pragma unroll
+                for (int p = 0; p < XPLANES; ++p) dst[4 * p + q] = word[p];
+                if (q == 0) {
+                    wsum[j * units + U] = sx;
+                    wscl[j * units + U] = ldexpf(1.f, -E);
+                }
             }
         }
         // the same wave reads these LDS words next: order the writes before the reads
@@ -553,23 +532,13 @@ __global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R)
 // One token: block = one wave per work item on rows [row0, row0+R) of Wd
 // (R = 64/S, S lane slices of upl units, so every expert's rows of this
 // tile are requested at once).  With no resident mask item w is slot w (the
-// shared expert slot k), so the h digit planes are staged by direct loads
-// before the work list is read; the combine inputs load meanwhile too.
+// shared expert slot k), so h is loaded before the work list is read; the
+// combine inputs load meanwhile too.
 // Then out = y_shared + sum_{r asc, resident} gate[r] * y[slot(r)] and
 // x_next = x + out for those rows.
 __host__ __device__ inline int down_one_lds_words(int k, int f, int R) {
     const int S = 64 / R, units = f / 32;
     return (k + 1) * R + (k + 1) * (units * XPLANES * 4 + S * 4 + 2 * units) + 3 * k;
-}
-
-__device__ __forceinline__ void down_one_stage(const LayerArgs &a, int slot, uint32_t *wdig, int S, int upl) {
-    const int lane = threadIdx.x & 63, units = a.f / 32, chunks = upl * XPLANES;
-    for (int sl = 0; sl < S; ++sl) {
-        const int c = lane;
-        const uint32_t *src = a.hq + ((size_t)slot * units + sl * upl) * XPLANES * 4 + 4 * min(c, chunks - 1);
-        uint32_t *dst = wdig + dig_off(sl * upl, upl);
-        if (c < chunks) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-    }
 }
 
 template <int BITS>
@@ -589,13 +558,8 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
     int *con = cp + k;                                                       // [k] resident
     const bool fast = a.mask == nullptr;
     int slot = wave < k ? wave : k;
-    if (fast) down_one_stage(a, slot, wdig, S, upl);
-    int sv = 0;
-    float cv = 0.f;
-    if (fast && lane < units) {
-        sv = a.hsum[(size_t)slot * units + lane];
-        cv = a.hscl[(size_t)slot * units + lane];
-    }
+    HStage<1> st;
+    if (fast) st.load(a, slot);
     int pe = 0, pp = 0;
     float pg = 0.f;
     if (wave == 0 && lane < k) {
@@ -608,22 +572,12 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
         const WorkItem it = a.items[wave];
         if (!fast) {
             slot = it.slot0;
-            down_one_stage(a, slot, wdig, S, upl);
-            if (lane < units) {
-                sv = a.hsum[(size_t)slot * units + lane];
-                cv = a.hscl[(size_t)slot * units + lane];
-            }
+            st.load(a, slot);
         }
         UTile<BITS> wt;
         wt.load(a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
                 a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
-        if (lane < units) {
-            wsum[lane] = sv;
-            wscl[lane] = cv;
-        }
-        // this wave's staged planes have landed and its LDS writes precede its reads
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_wave_barrier();
+        st.store(a, upl, dstride, wdig, wsum, wscl);
         float res[1];
         utile_compute<BITS, 1>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, nullptr, res);
         if (lane < R) ybuf[slot * R + lane] = res[0];
@@ -705,8 +659,10 @@ template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_i
     const int nt = nt_round(ntmax_for(a.T));
     const int off = gateup_lds_words(a.d, R, a.T, nt);
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
-    const dim3 grid(max_items * (a.f / 32) + 1);
-    LAUNCH_NT(gemv_gateup_small_kernel, BITS, nt, grid, 64 * 2 * (32 / R), lds, s, a, R, off);
+    const int G = (a.T == 1 || a.f % (4 * R)) ? 1 : 4;   // row groups per block
+    const dim3 grid(max_items * (a.f / (G * R)) + 1);
+    if (nt == 1 && G != 1) return hipErrorInvalidValue;
+    LAUNCH_NT(gemv_gateup_small_kernel, BITS, nt, grid, 128 * G, lds, s, a, R, off);
     return hipGetLastError();
 }
 

@@ -104,115 +104,6 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
     *z_out = __uint_as_float((my_k & 0x80000000u) ? (my_k & 0x7FFFFFFFu) : ~my_k);
 }
 
-// Ordered top-k by threshold: tau = the k-th largest value key (bitwise
-// search, each step counting keys >= candidate with one ballot per
-// candidate slot), the picks are the keys above tau plus the lowest-index
-// keys equal to tau, and each pick's place in (value desc, index asc) order
-// is its rank among the picks.  Same contract as wave_topk_picks_fast; with
-// sel[j] (optional) = the 64-bit ballot of picked experts 64j .. 64j+63.
-template <int JM>
-__device__ __forceinline__ void wave_topk_picks_tau(const float *z, int E, int k, float scale, const float *bias,
-                                                    int *e_out, float *z_out, uint64_t *sel) {
-    const int lane = threadIdx.x & 63;
-    float zv[JM], bv[JM];
-#pragma unroll
-    for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
-#pragma unroll
-    for (int j = 0; j < JM; ++j) bv[j] = 0.f;
-    if (bias) {
-#pragma unroll
-        for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
-    }
-    uint32_t kv[JM];   // value keys, 0 for slots past E (below every real key)
-#pragma unroll
-    for (int j = 0; j < JM; ++j) kv[j] = (lane + 64 * j < E) ? f32_key(zv[j] * scale + bv[j]) : 0u;
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < JM; ++j) cnt += __popcll(__ballot(kv[j] >= cand));
-        if (cnt >= k) tau = cand;
-    }
-    // picks: keys above tau, then ties at tau in index order (j asc, lane asc)
-    uint64_t pick[JM];
-    int rem = k;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        pick[j] = __ballot(kv[j] > tau);
-        rem -= __popcll(pick[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        uint64_t eq = __ballot(kv[j] == tau);
-        while (rem > 0 && eq) {
-            const uint64_t low = eq & (~eq + 1ull);
-            pick[j] |= low;
-            eq ^= low;
-            --rem;
-        }
-    }
-    if (sel) {
-#pragma unroll
-        for (int j = 0; j < JM; ++j) sel[j] = pick[j];
-    }
-    // pick r (in index order) -> lane r; its rank by (value desc, index asc)
-    int my_e = 0, pe = -1;
-    uint32_t pk = 0;
-    int r = 0;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        const bool mine = (pick[j] >> lane) & 1ull;
-        const int before = r + __popcll(pick[j] & ((1ull << lane) - 1ull));
-        // lane `before` receives this pick: gather via LDS-free shuffles below
-        if (mine) { pe = before; }
-        r += __popcll(pick[j]);
-        (void)my_e;
-    }
-    // move (e, key) of every pick to lane `rank-in-index-order` with ds_bpermute-free loops
-    int ie = 0;
-    uint32_t ik = 0;
-#pragma unroll
-    for (int j = 0; j < JM; ++j) {
-        uint64_t m = pick[j];
-        int base = 0;
-#pragma unroll
-        for (int jj = 0; jj < JM; ++jj) base += jj < j ? __popcll(pick[jj]) : 0;
-        while (m) {
-            const int src = __ffsll((unsigned long long)m) - 1;
-            m &= m - 1ull;
-            const uint32_t kk = (uint32_t)__builtin_amdgcn_readlane((int)kv[j], src);
-            if (lane == base) {
-                ie = src + 64 * j;
-                ik = kk;
-            }
-            ++base;
-        }
-    }
-    (void)pe;
-    // rank of the pick held by lane r < k
-    int rank = 0;
-    for (int q = 0; q < k; ++q) {
-        const uint32_t qk = (uint32_t)__shfl((int)ik, q, WAVE);
-        const int qe = __shfl(ie, q, WAVE);
-        rank += (qk > ik || (qk == ik && qe < ie)) ? 1 : 0;
-    }
-    // lane `rank` takes the pick
-    int oe = 0;
-    uint32_t ok = 0x80000000u;
-    for (int q = 0; q < k; ++q) {
-        const int qr = __shfl(rank, q, WAVE);
-        const int qe = __shfl(ie, q, WAVE);
-        const uint32_t qk = (uint32_t)__shfl((int)ik, q, WAVE);
-        if (lane == qr) {
-            oe = qe;
-            ok = qk;
-        }
-    }
-    *e_out = oe;
-    *z_out = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
-}
-
 // Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
 __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float scale, const float *bias,
                                           int32_t *idx_out, float *gate_out, int32_t *idx_out2, float *gate_out2,
