@@ -1,21 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X sparse MoE layer forward.
 
-Workload (one step = one full layer forward: router, top-k and gates,
-permutation, expert FFNs over packed 3-bit blocks, shared expert, combine):
-the full-size decode layer -- 512 routed experts top-10 + 1 shared,
-d = 2048, f = 768, 3-bit 256-element blocks, T = 1 token of bf16 N(0,1)
-input, random N(0, 1/d) router.  Every step uses a new token and the next of
-`--rotate` independent resident layers, so the ~0.93 GB of codes per layer
-come from HBM, not from the 256 MB Infinity Cache.
+Default workload (the headline line; one step = one full layer forward:
+router, top-k and gates, permutation, expert FFNs over packed 3-bit blocks,
+shared expert, combine): the full-size decode layer -- 512 routed experts
+top-10 + 1 shared, d = 2048, f = 768, 3-bit 256-element blocks, T = 1 token
+of bf16 N(0,1) input, random N(0, 1/d) router.  Every step uses a new token
+and the next of `--rotate` independent resident layers, so the ~0.93 GB of
+codes per layer come from HBM, not from the 256 MB Infinity Cache.
 
-Prints one JSON line: tokens/s, the dominant kernel's HBM roofline fraction
-(kernel time from HIP events recorded by the library around that kernel) and
-the CPU oracle's rate on a bounded sample.
+`--workload prefill_2bit` times the 4096-token 2-bit prefill chunk instead
+(matrix-core GEMM path); it is a profiling aid, not the headline line.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline fraction
+(kernel time from HIP events the library records around that kernel, on the
+stream the kernel runs on) with its HBM bytes from committed rocprofv3
+counter runs when they were taken on the current kernel source, and the CPU
+oracle's rate on a bounded sample.
+
+`--copy-calibration MIB` adds a plain fp32 elementwise copy of known size to
+the run (reference kernel for the byte counters); `--traffic-from FETCH
+WRITE` turns the counter CSVs of two such runs (rocprofv3 --pmc FETCH_SIZE,
+then WRITE_SIZE) into profiles/traffic_<kernel>_<workload>.md.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -27,22 +39,58 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
+
+# Per workload: the dominant kernel (library kernel name and the symbol
+# rocprofv3 reports) and the source files that define it.
+WORKLOADS = {
+    "decode": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=16, inputs=None,
+                   sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
+    "prefill_2bit": dict(kernel="gemm_gateup", symbol="gemm_gateup_kernel", rotate=2, inputs=4,
+                         sources=["common.hpp", "mfma.hpp", "gemm_impl.hpp", "gemm_gu2.hip"]),
+}
+COPY_SYMBOL = "MulFunctor"
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--rotate", type=int, default=16, help="independent resident layers cycled through")
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default 2000 decode, 200 prefill)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps (default steps / 10)")
+    p.add_argument("--rotate", type=int, default=None, help="independent resident layers cycled through")
     p.add_argument("--cpu-sample-s", type=float, default=12.0, help="target seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-only", action="store_true", help="skip the CPU baseline and event pass")
-    return p.parse_args()
+    p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS),
+                   help="decode (the headline line) or the 4096-token 2-bit prefill chunk")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run a plain fp32 elementwise copy of MIB MiB (read + write) 5 times before the warmup")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the traffic summary from two rocprofv3 counter CSVs of a --copy-calibration run")
+    a = p.parse_args()
+    if a.steps is None:
+        a.steps = 2000 if a.workload == "decode" else 200
+    if a.warmup is None:
+        a.warmup = max(1, a.steps // 10)
+    if a.rotate is None:
+        a.rotate = WORKLOADS[a.workload]["rotate"]
+    return a
+
+
+def source_hash(workload):
+    h = hashlib.sha256()
+    for name in WORKLOADS[workload]["sources"]:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the MoE layer path here is single-GPU "
               "(expert-parallel sharding is a design note, not built); use --gpus 1", file=sys.stderr)
@@ -52,12 +100,14 @@ def main():
     import bit_routed_expert_amd as brx
     import synth
 
-    w = synth.WORKLOADS["decode"]
-    T, E, k, d, f = w.tokens, w.n_experts, w.top_k, w.d_model, w.d_ff
+    cfg = WORKLOADS[args.workload]
+    w = synth.WORKLOADS[args.workload]
+    T = w.tokens_per_call
+    E, k, d, f = w.n_experts, w.top_k, w.d_model, w.d_ff
     sh = brx.shape(E, k, d, f, w.bits)
     dev = torch.device("cuda", 0)
 
-    # ---- resident inputs: `rotate` independent layers + one token per step
+    # ---- resident inputs: `rotate` independent layers + the token batches
     nrot = args.rotate
     layer_bytes = w.experts_total * w.code_bytes_per_expert
     pinned = torch.empty(layer_bytes, dtype=torch.uint8, pin_memory=True)
@@ -71,8 +121,9 @@ def main():
         wr = torch.from_numpy(synth.router_weights(w, l)).to(dev)
         layers.append(brx.LayerData(router_w=wr, codes=codes, scales=scales))
     del pinned
-    n_tok = args.warmup + args.steps
-    xs = torch.from_numpy(synth.x_tokens(w, range(n_tok), rep=1).view(np.int16)).to(dev)
+    n_step = args.warmup + args.steps
+    n_in = n_step if cfg["inputs"] is None else cfg["inputs"]   # a new token per decode step
+    xs = torch.from_numpy(synth.x_tokens(w, range(n_in * T), rep=1).view(np.int16)).to(dev).view(n_in, T, d)
     setup_s = time.time() - t0
 
     ws_bytes = brx.workspace_bytes(sh, T, 1)
@@ -83,9 +134,16 @@ def main():
     names = brx.kernel_names(sh, T)
 
     def step(i, events=None):
-        brx.forward(sh, [layers[i % nrot]], xs[i], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
+        brx.forward(sh, [layers[i % nrot]], xs[i % n_in], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
                     events=events, stream=stream)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -94,7 +152,7 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for i in range(args.warmup, n_tok):
+    for i in range(args.warmup, n_step):
         step(i)
     ev1.record()
     torch.cuda.synchronize()
@@ -109,7 +167,7 @@ def main():
         hip = _Hip()
         evs = [[hip.event() for _ in range(2 * nk)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        for j, i in enumerate(range(args.warmup, n_tok)):
+        for j, i in enumerate(range(args.warmup, n_step)):
             step(i, events=evs[j])
         torch.cuda.synchronize()
         for j in range(args.steps):
@@ -120,32 +178,45 @@ def main():
                 hip.destroy(e)
     kern_avg = {n: (float(np.mean(v)) if v else None) for n, v in kern_us.items()}
 
-    # dominant kernel: the gate/up expert kernel (it also takes the top-k from
-    # the logits).  Algorithmic bytes per launch: the gate and up codes + fp16
-    # scales of the 11 experts one token needs (logits and activations are
-    # a few KB and are left out).
-    per_expert_gu = 2 * (d * f * w.bits // 8 + (d * f // 256) * 2)
-    n_exp = k + 1
-    dom = "route_gemv_gateup"
-    dom_bytes = n_exp * per_expert_gu
+    per_mat_codes = d * f * w.bits // 8 + (d * f // 256) * 2   # one matrix: codes + fp16 scales
+    dom = cfg["kernel"]
     dom_us = kern_avg.get(dom)
     roof = None
-    if dom_us:
-        achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": dom_bytes, "avg_us": round(dom_us, 3)}
-        roof["traffic"] = _traffic_from_profiles(dom)
-
-    # whole-layer algorithmic bytes: 11 experts (3 matrices) + router + x + y
-    layer_bytes_alg = n_exp * (3 * d * f * w.bits // 8 + 3 * (d * f // 256) * 2) + E * d * 4 + d * 2 + d * 4
+    if args.workload == "decode":
+        # gate and up codes + scales of the 11 experts one token needs (logits
+        # and activations are a few KB and are left out)
+        n_exp = k + 1
+        dom_bytes = n_exp * 2 * per_mat_codes
+        if dom_us:
+            achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+            roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": _traffic_from_profiles(args.workload), "algorithmic_bytes": dom_bytes,
+                    "avg_us": round(dom_us, 3)}
+        layer_bytes_alg = n_exp * 3 * per_mat_codes + E * d * 4 + d * 2 + d * 4
+        metric = "MoE-layer tokens/s (decode T=1, full-size 3-bit layer)"
+        wl = "decode layer: E=512 top-10 + 1 shared, d=2048, f=768, 3-bit blocks, T=1"
+        dtype = "int4-dot/fp32"
+    else:
+        # useful gate+up flops of the T*k routed and T shared token-expert pairs
+        flops = 2.0 * (T * k + T) * d * (2 * f)
+        if dom_us:
+            achieved = flops / (dom_us * 1e-6) / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": _traffic_from_profiles(args.workload), "algorithmic_flops": flops,
+                    "avg_us": round(dom_us, 3)}
+        layer_bytes_alg = (E + 1) * 3 * per_mat_codes + E * d * 4 + T * d * 2 + T * d * 4
+        metric = "MoE-layer tokens/s (4096-token prefill chunk, 2-bit layer)"
+        wl = "prefill chunk: E=512 top-10 + 1 shared, d=2048, f=768, 2-bit blocks, T=4096"
+        dtype = "bf16-mfma/fp32"
 
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
         cpu = _cpu_baseline(w, args.cpu_sample_s)
 
     rec = {
-        "metric": "MoE-layer tokens/s (decode T=1, full-size 3-bit layer)",
+        "metric": metric,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -155,10 +226,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4-dot/fp32",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "decode layer: E=512 top-10 + 1 shared, d=2048, f=768, 3-bit blocks, T=1",
-                   "tokens_per_step": T, "resident_layers_rotated": nrot, "parallelism": "single GPU"},
+        "config": {"workload": wl, "tokens_per_step": T, "resident_layers_rotated": nrot,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "layer_hbm_frac": round(layer_bytes_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {n: (round(v, 3) if v is not None else None) for n, v in kern_avg.items()},
@@ -197,30 +268,84 @@ class _Hip:
         self.lib.hipEventDestroy(e)
 
 
-def _traffic_from_profiles(kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, only if they
-    were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_decode.json")
+def _traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{WORKLOADS[workload]['kernel']}_{workload}.md")
+
+
+def _traffic_from_profiles(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, only if it was taken on the current kernel source."""
+    path = _traffic_path(workload)
     if not os.path.exists(path):
         return None
-    try:
-        import hashlib
-        rec = json.load(open(path))
-        src = os.path.join(ROOT, "bit_routed_expert_amd", "csrc", rec["source"])
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if h != rec["source_sha256"]:
-            return None
-        return rec["bytes_per_launch"]
-    except Exception:
-        return None
+    for line in open(path):
+        if line.startswith("TRAFFIC "):
+            rec = json.loads(line[len("TRAFFIC "):])
+            if rec.get("source_sha256") != source_hash(workload):
+                return None
+            return rec["bytes_per_launch"]
+    return None
+
+
+def _counter_rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def traffic_summary(args):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel,
+    scaled by what the same counters read for the calibration copy (which
+    moves exactly MIB MiB each way)."""
+    if not args.copy_calibration:
+        sys.exit("--traffic-from needs the --copy-calibration size of the profiled run")
+    cfg = WORKLOADS[args.workload]
+    copy_bytes = args.copy_calibration * (1 << 20)
+    out = {}
+    for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.traffic_from):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
+        cp = [float(r["Counter_Value"]) for r in rows if COPY_SYMBOL in r["Kernel_Name"]]
+        kv = [float(r["Counter_Value"]) for r in rows if cfg["symbol"] in r["Kernel_Name"]]
+        if not cp or not kv:
+            sys.exit(f"{path}: no {counter} rows for the calibration copy or {cfg['symbol']}")
+        factor = copy_bytes / (float(np.median(cp)) * 1024.0)
+        out[counter] = dict(kib_per_dispatch=float(np.mean(kv)), dispatches=len(kv),
+                            copy_kib=float(np.median(cp)), factor=factor,
+                            bytes=float(np.mean(kv)) * 1024.0 * factor)
+    rec = dict(kernel=cfg["kernel"], symbol=cfg["symbol"], workload=args.workload,
+               fetch_bytes=round(out["FETCH_SIZE"]["bytes"]), write_bytes=round(out["WRITE_SIZE"]["bytes"]),
+               bytes_per_launch=round(out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]),
+               fetch_factor=round(out["FETCH_SIZE"]["factor"], 4), write_factor=round(out["WRITE_SIZE"]["factor"], 4),
+               copy_mib=args.copy_calibration, source_sha256=source_hash(args.workload))
+    path = _traffic_path(args.workload)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of `{cfg['kernel']}` ({args.workload} workload)\n\n")
+        fh.write("Counters: rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch), one run each, on\n"
+                 f"`bench.py --workload {args.workload} --profile-only --copy-calibration {args.copy_calibration}`;"
+                 " every value is scaled by\nexpected / measured for the calibration copy"
+                 f" (`torch.mul(src, 1.0, out=dst)`, {args.copy_calibration} MiB each way).\n\n")
+        fh.write("| counter | kernel KiB/dispatch | dispatches | copy KiB | factor | bytes/launch |\n|---|---|---|---|---|---|\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            o = out[c]
+            fh.write(f"| {c} | {o['kib_per_dispatch']:.1f} | {o['dispatches']} | {o['copy_kib']:.1f} | "
+                     f"{o['factor']:.4f} | {o['bytes']:.0f} |\n")
+        fh.write("\nCommands (from the repository root; each counter pass in its own run):\n\n```\n")
+        for c, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            fh.write(f"cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv "
+                     f"-d $REPO/gpurun_out/pmc_{tag} -o run -- python3 $REPO/bench.py --workload {args.workload} "
+                     f"--steps 50 --warmup 10 --profile-only --copy-calibration {args.copy_calibration}\n")
+        fh.write(f"python3 bench.py --workload {args.workload} --copy-calibration {args.copy_calibration} "
+                 "--traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
+                 "gpurun_out/pmc_write/run_counter_collection.csv\n```\n\n")
+        fh.write("TRAFFIC " + json.dumps(rec) + "\n")
+    print(json.dumps(rec))
 
 
 def _cpu_baseline(w, target_s):
     """The oracle (grouped evaluation: each needed expert dequantised once,
-    then its tokens) on single decode tokens, for about target_s seconds."""
+    then its tokens) on a bounded sample of the workload's tokens, for about
+    target_s seconds."""
     import oracle
     import synth
-    L = {}
     codes = np.empty(w.experts_total * w.code_bytes_per_expert, dtype=np.uint8)
     synth.layer_codes_into(w, 0, codes.ctypes.data)
     scales = synth.layer_scales(w, 0)
@@ -237,7 +362,7 @@ def _cpu_baseline(w, target_s):
     el = time.time() - t0
     cores = oracle._threads()
     return {"value": round(n / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} decode tokens, one full-size layer each (grouped oracle, {cores} threads)"}
+            "sample": f"{n} tokens, one full-size layer each (grouped oracle, {cores} threads)"}
 
 
 if __name__ == "__main__":
