@@ -12,6 +12,14 @@ namespace {
 
 thread_local hipError_t g_last_hip = hipSuccess;
 
+}  // namespace
+
+namespace strata {
+thread_local LaunchEvents g_launch_events;
+}  // namespace strata
+
+namespace {
+
 constexpr size_t ALIGN = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -129,15 +137,16 @@ void set_route_out(LayerArgs &a, const strata_route_out *r) {
     a.u_pos = r->pos;
 }
 
+// Caller events around each kernel group, attached to its launches.
 struct Recorder {
     void *const *events;
     int n, i;
     hipStream_t s;
     void before() {
-        if (events && i < n) (void)hipEventRecord((hipEvent_t)events[2 * i], s);
+        if (events && i < n) g_launch_events = LaunchEvents{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
     }
     void after() {
-        if (events && i < n) (void)hipEventRecord((hipEvent_t)events[2 * i + 1], s);
+        g_launch_events = LaunchEvents{};
         ++i;
     }
 };

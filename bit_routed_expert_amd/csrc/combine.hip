@@ -73,9 +73,9 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s) {
     const int blocks = a.T * ((a.d + CB_COLS - 1) / CB_COLS);
     if (a.x_is_bf16)
-        hipLaunchKernelGGL(combine_kernel<1>, dim3(blocks), dim3(256), 0, s, a);
+        STRATA_LAUNCH(combine_kernel<1>, dim3(blocks), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(combine_kernel<0>, dim3(blocks), dim3(256), 0, s, a);
+        STRATA_LAUNCH(combine_kernel<0>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

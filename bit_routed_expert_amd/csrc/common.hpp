@@ -2,6 +2,7 @@
 // gfx950 only (64-wide wavefronts).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace strata {
@@ -149,6 +150,22 @@ struct LayerArgs {
     float *x_next;       // [T][d] residual stream after this layer (nullable)
     int route_only;
 };
+
+// Optional HIP events around the next kernels of the calling thread: the
+// first launch records `start` when it begins, every launch records `stop`
+// when it ends (so after a group of launches `stop` marks the last one),
+// both timed by the dispatch itself rather than by separate queue packets.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+#define STRATA_LAUNCH(KER, GRID, BLOCK, LDS, STREAM, ...)                                                 \
+    do {                                                                                                  \
+        hipEvent_t ev0_ = g_launch_events.start;                                                          \
+        g_launch_events.start = nullptr;                                                                  \
+        hipExtLaunchKernelGGL(KER, GRID, BLOCK, LDS, STREAM, ev0_, g_launch_events.stop, 0, __VA_ARGS__); \
+    } while (0)
 
 // Launchers (one file each); return hipGetLastError() of their launches.
 hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);

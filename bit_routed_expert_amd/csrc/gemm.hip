@@ -71,7 +71,7 @@ bool gemm_supported(int d, int f) {
 }
 
 hipError_t launch_gemm_prep(const LayerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(gemm_prep_kernel, dim3(a.T), dim3(256), 0, s, a);
+    STRATA_LAUNCH(gemm_prep_kernel, dim3(a.T), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

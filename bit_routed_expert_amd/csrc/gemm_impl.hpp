@@ -463,14 +463,14 @@ __global__ __launch_bounds__(256, 2) void gemm_down_kernel(LayerArgs a, int nft)
 template <int BITS, int PASSES> hipError_t gemm_gateup_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int nft = a.f / 128;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_gateup_kernel<BITS, PASSES>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
+    STRATA_LAUNCH((gemm_gateup_kernel<BITS, PASSES>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
     return hipGetLastError();
 }
 
 template <int BITS> hipError_t gemm_down_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int nft = (a.d + 255) / 256;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
+    STRATA_LAUNCH((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
     return hipGetLastError();
 }
 

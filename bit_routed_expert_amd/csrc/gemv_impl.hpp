@@ -646,11 +646,11 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
     do {                                                                                             \
         if ((lds) > LDS_LIMIT) return hipErrorInvalidValue;                                          \
         switch (nt) {                                                                                \
-            case 1: hipLaunchKernelGGL((KER<BITS, 1>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 2: hipLaunchKernelGGL((KER<BITS, 2>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 4: hipLaunchKernelGGL((KER<BITS, 4>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 5: hipLaunchKernelGGL((KER<BITS, 5>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            default: hipLaunchKernelGGL((KER<BITS, 8>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
+            case 1: STRATA_LAUNCH((KER<BITS, 1>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
+            case 2: STRATA_LAUNCH((KER<BITS, 2>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
+            case 4: STRATA_LAUNCH((KER<BITS, 4>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
+            case 5: STRATA_LAUNCH((KER<BITS, 5>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
+            default: STRATA_LAUNCH((KER<BITS, 8>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
         }                                                                                            \
     } while (0)
 
@@ -696,7 +696,7 @@ template <int BITS> hipError_t down_rows_launch(const LayerArgs &a, hipStream_t 
     if (a.T == 1) {
         const size_t lds1 = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
         if (lds1 > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(gemv_down_rows_one_kernel<BITS>, grid, dim3(64 * (a.k + 1)), lds1, s, a, R);
+        STRATA_LAUNCH(gemv_down_rows_one_kernel<BITS>, grid, dim3(64 * (a.k + 1)), lds1, s, a, R);
         return hipGetLastError();
     }
     LAUNCH_NT(gemv_down_rows_kernel, BITS, nt, grid, 64 * nw, lds, s, a, R);

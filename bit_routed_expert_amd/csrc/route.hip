@@ -427,16 +427,16 @@ hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s) {
     const size_t lds = sizeof(float) * (size_t)a.T * a.d;
     if (lds > LDS_LIMIT) return hipErrorInvalidValue;
     if (a.x_is_bf16)
-        hipLaunchKernelGGL(route_logits_small_kernel<1>, dim3(blocks), dim3(256), lds, s, a);
+        STRATA_LAUNCH(route_logits_small_kernel<1>, dim3(blocks), dim3(256), lds, s, a);
     else
-        hipLaunchKernelGGL(route_logits_small_kernel<0>, dim3(blocks), dim3(256), lds, s, a);
+        STRATA_LAUNCH(route_logits_small_kernel<0>, dim3(blocks), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
     const size_t lds = 4 * (size_t)small_route_lds_words(a.E);
     if (lds > LDS_LIMIT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_small_finish_kernel, dim3(1), dim3(256), lds, s, a);
+    STRATA_LAUNCH(route_small_finish_kernel, dim3(1), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -444,14 +444,14 @@ hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
     const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T);
     if (a.d % RT_K) return hipErrorInvalidValue;
     if (a.x_is_bf16)
-        hipLaunchKernelGGL(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
+        STRATA_LAUNCH(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(route_logits_mfma_kernel<3>, grid, dim3(256), 0, s, a);
+        STRATA_LAUNCH(route_logits_mfma_kernel<3>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+    STRATA_LAUNCH(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -462,9 +462,9 @@ hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s) {
     if (a.E > 1024) return hipErrorInvalidValue;
     const size_t lds = 4 * ((size_t)a.E * (PERM_T / 32) + a.E + 16);
     if (lds > LDS_LIMIT) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_count_kernel, dim3(nb), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, a, nb, tile);
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(256), lds, s, a);
+    STRATA_LAUNCH(route_count_kernel, dim3(nb), dim3(256), 0, s, a);
+    STRATA_LAUNCH(route_scan_kernel, dim3(1), dim3(1024), 0, s, a, nb, tile);
+    STRATA_LAUNCH(route_scatter_kernel, dim3(nb), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
