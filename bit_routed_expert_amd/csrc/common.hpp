@@ -50,13 +50,26 @@ template <int P> __device__ __forceinline__ int fixed_point_exponent(float max_a
     return E;
 }
 
-// Balanced base-16 digits of X (|X| <= digit_limit(P)), least significant first.
-template <int P> __device__ __forceinline__ void to_digits(int X, int d[P]) {
+// Digit-plane words of 8 fixed-point values X[n] (|X| <= digit_limit(6)):
+// word[p] nibble n = balanced digit p of X[n] as a signed 4-bit field.
+// Y = X + 0x888888 has plain base-16 digits d_p + 8, so each field is
+// nibble p of Y xor 8; the nibbles are moved into place with byte permutes.
+__device__ __forceinline__ void digit_words(const int X[8], uint32_t word[6]) {
+    uint32_t ev[4], od[4];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        int v = ((X + 8) & 15) - 8;
-        d[p] = v;
-        X = (X - v) >> 4;
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t y0 = (uint32_t)(X[2 * q] + 0x888888), y1 = (uint32_t)(X[2 * q + 1] + 0x888888);
+        ev[q] = (y0 & 0x0F0F0Fu) | ((y1 & 0x0F0F0Fu) << 4);          // byte b: nibble 2b of values 2q, 2q+1
+        od[q] = ((y0 >> 4) & 0x0F0F0Fu) | (((y1 >> 4) & 0x0F0F0Fu) << 4);
+    }
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+        const uint32_t lo_sel = (uint32_t)b | ((uint32_t)(b + 4) << 8) | 0x0C0C0000u;
+        const uint32_t hi_sel = 0x00000C0Cu | ((uint32_t)b << 16) | ((uint32_t)(b + 4) << 24);
+        word[2 * b] = (__builtin_amdgcn_perm(ev[1], ev[0], lo_sel) | __builtin_amdgcn_perm(ev[3], ev[2], hi_sel)) ^
+                      0x88888888u;
+        word[2 * b + 1] =
+            (__builtin_amdgcn_perm(od[1], od[0], lo_sel) | __builtin_amdgcn_perm(od[3], od[2], hi_sel)) ^ 0x88888888u;
     }
 }
 

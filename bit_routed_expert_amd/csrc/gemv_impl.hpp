@@ -212,18 +212,14 @@ __host__ __device__ inline int unit_period(int in, int upg) {
 // Quantise 8 consecutive values with exponent E into one word per digit
 // plane (nibble n = digit of value n); returns the sum of the fixed-point values.
 __device__ __forceinline__ int chunk_digits(const float v[8], int E, uint32_t word[XPLANES]) {
-    int sx = 0;
-#pragma unroll
-    for (int p = 0; p < XPLANES; ++p) word[p] = 0;
+    static_assert(XPLANES == 6, "digit_words packs six planes");
+    int X[8], sx = 0;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-        const int X = (int)rintf(ldexpf(v[n], E));
-        sx += X;
-        int dg[XPLANES];
-        to_digits<XPLANES>(X, dg);
-#pragma unroll
-        for (int p = 0; p < XPLANES; ++p) word[p] |= ((uint32_t)dg[p] & 15u) << (4 * n);
+        X[n] = (int)rintf(ldexpf(v[n], E));
+        sx += X[n];
     }
+    digit_words(X, word);
     return sx;
 }
 

@@ -58,15 +58,7 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
             sx += X[n];
         }
         uint32_t word[XPLANES];
-#pragma unroll
-        for (int p = 0; p < XPLANES; ++p) word[p] = 0;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            int dg[XPLANES];
-            to_digits<XPLANES>(X[n], dg);
-#pragma unroll
-            for (int p = 0; p < XPLANES; ++p) word[p] |= ((uint32_t)dg[p] & 15u) << (4 * n);
-        }
+        digit_words(X, word);
         // digit sums per 32-column unit (4 consecutive chunks)
         sx += __shfl_xor(sx, 1, WAVE);
         sx += __shfl_xor(sx, 2, WAVE);
