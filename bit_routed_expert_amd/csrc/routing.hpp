@@ -35,9 +35,9 @@ template <bool MAX> __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t
 // Ordered top-k of E logits z[e] * scale + bias[e] by one wave (JM = E/64
 // rounded up to 8 or 16); lane r < k ends with pick r: *e_out, *z_out.  Each
 // lane sorts its JM candidates by (value desc, index asc); a round takes the
-// wave maximum of the lanes'
-// head values (32-bit) and, only when several lanes hold that value, the
-// smallest of their head indices; the owning lane pops its head.
+// wave maximum of the lanes' head values (32-bit) and, only when several
+// lanes hold that value, the smallest of their head indices; the owning
+// lane pops its head.
 template <int JM>
 __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
                                                      int *e_out, float *z_out) {
