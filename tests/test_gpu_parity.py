@@ -104,21 +104,107 @@ def test_decode_repeat_is_bitwise_identical():
     np.testing.assert_array_equal(a["y"], b["y"])
 
 
-def test_fp32_input_with_norm_first():
+@pytest.mark.parametrize("T", [3, 12])
+def test_fp32_input_with_norm_first(T):
+    """fp32 residual-stream input, RMS-normalised before routing: the decode
+    path (T = 3) and the matrix-core path with hi/lo bf16 activations (T = 12)."""
     w = synth.WORKLOADS["decode"]
     L = W.layer_data(w, 0)
-    rng = np.random.default_rng(11)
+    rng = np.random.default_rng(11 + T)
     # fp32 residual-stream input of a later layer: redraw rows until the margins hold
     xs = []
-    while len(xs) < 3:
+    while len(xs) < T:
         xr = (7.0 * rng.standard_normal(w.d_model)).astype(np.float32)
         u = oracle.rmsnorm(xr[None])
         if oracle.topk_margin(oracle.logits(u, L["Wr"]), w.top_k)[0] >= W.MARGIN:
             xs.append(xr)
     x = np.stack(xs)
     u = oracle.rmsnorm(x)
+    print(f"case fp32 input T={T}", flush=True)
     ref = _oracle_layer(w, L, u)
-    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 1, 3, flags=1)
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 1, T, flags=1)
     G.assert_route_equal(got["route"][0], ref)
     G.assert_close(got["y"], ref["out"])
     np.testing.assert_array_equal(got["resid"], (x + got["y"]).astype(np.float32))
+
+
+def _perturb_scales(scales: np.ndarray, seed: int) -> np.ndarray:
+    """Every 10th block (seeded) gets a zero scale (+0 or -0), every other
+    10th a negated one."""
+    s = scales.copy()
+    rng = np.random.default_rng(seed)
+    r = rng.random(s.shape)
+    s[r < 0.05] = 0x0000
+    s[(r >= 0.05) & (r < 0.1)] = 0x8000
+    neg = (r >= 0.1) & (r < 0.2)
+    s[neg] ^= 0x8000
+    return s
+
+
+@pytest.mark.parametrize("name,bits,T", [("tiny", 3, 3), ("tiny", 2, 3), ("tiny", 3, 20), ("tiny", 2, 20),
+                                         ("decode", 3, 1), ("decode", 3, 9)])
+def test_zero_and_negative_block_scales(name, bits, T):
+    """Blocks with zero (or -0) scales contribute nothing and negative scales
+    flip their block, on the decode GEMV path (T <= 8) and on the matrix-core
+    path (T > 8), whose scale folding treats zero scales separately."""
+    w, L, x, T = _layer_case(name, T=T, rep=5, bits=bits)
+    L["scales"] = _perturb_scales(L["scales"], 99 + T + bits)
+    print(f"case {name} bits={bits} T={T} perturbed scales", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_three_layer_stack_on_matrix_core_path(bits):
+    """L = 3, T = 20 on the small layer: layers 1 and 2 take the normalised
+    fp32 residual stream (hi/lo bf16 activations on the matrix cores).  Ids
+    bit-exact against the oracle's chain; gates against the oracle run on the
+    GPU's own layer input (chained one-layer calls, equal to the stack
+    bitwise); y_2 and x_3 within tolerance."""
+    w = synth.WORKLOADS["tiny"]
+    if bits != w.bits:
+        w = synth.Workload(w.name + f"_b{bits}", w.n_experts, w.top_k, w.d_model, w.d_ff, bits, w.tokens,
+                           seed=w.seed + 0x100)
+    T, nl = 20, 3
+    t = G.torch()
+    Ls, refs = [], []
+    x0 = None
+    xl = None
+    for l in range(nl):
+        attempt = 0
+        while True:
+            Lr = W.layer_data(w, l, attempt)
+            if l == 0:
+                x0, _ = W.draw_tokens(w, Lr["Wr"], None, range(T), rep=21)
+                xl = synth.bf16_to_f32(x0)
+            u = oracle.layer_input(xl, l)
+            if oracle.topk_margin(oracle.logits(u, Lr["Wr"]), w.top_k).min() >= W.MARGIN:
+                break
+            attempt += 1
+        r = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, Lr["Wr"], Lr["codes"],
+                             Lr["scales"])
+        Ls.append(Lr)
+        refs.append(r)
+        y_last = r["out"]
+        xl = oracle.residual_add(xl, r["out"])
+    print(f"case 3-layer stack bits={bits} T={T}", flush=True)
+    dl = [G.layer_to_dev(L) for L in Ls]
+    got = G.run_forward(w, dl, G.dev(x0), 0, T)
+    G.assert_close(got["y"], y_last, what="y_2")
+    G.assert_close(got["resid"], xl, what="x_3")
+    xc, xd = G.dev(x0), 0
+    inputs = [synth.bf16_to_f32(x0)]
+    for l in range(nl):
+        one = G.run_forward(w, [dl[l]], xc, xd, T, flags=(1 if l > 0 else 0))
+        np.testing.assert_array_equal(one["route"][0]["topk_idx"], got["route"][l]["topk_idx"])
+        np.testing.assert_array_equal(one["route"][0]["topk_w"], got["route"][l]["topk_w"])
+        xc, xd = t.from_numpy(one["resid"]).cuda(), 1
+        inputs.append(one["resid"])
+    np.testing.assert_array_equal(one["resid"], got["resid"])
+    for l in range(nl):
+        np.testing.assert_array_equal(got["route"][l]["topk_idx"], refs[l]["idx"])
+        u_gpu = oracle.layer_input(inputs[l], l)
+        _, gate_g = oracle.select(oracle.logits(u_gpu, Ls[l]["Wr"]), w.top_k)
+        assert np.max(np.abs(got["route"][l]["topk_w"] - gate_g)) <= G.GATE_TOL, f"layer {l} gates"
