@@ -9,8 +9,12 @@ of bf16 N(0,1) input, random N(0, 1/d) router.  Every step uses a new token
 and the next of `--rotate` independent resident layers, so the ~0.93 GB of
 codes per layer come from HBM, not from the 256 MB Infinity Cache.
 
-`--workload prefill_2bit` times the 4096-token 2-bit prefill chunk instead
-(matrix-core GEMM path); it is a profiling aid, not the headline line.
+`--workload mtp_verify` times the verify step of multi-token prediction:
+5 tokens (1 accepted + 4 drafts) through a stack of 48 independent
+full-size 3-bit layers in one call, residual stream carried between layers
+(value = token-rows through the whole stack per second).  `--workload
+prefill_2bit` times the 4096-token 2-bit prefill chunk (matrix-core GEMM
+path).  Both are secondary lines; the decode layer is the headline.
 
 Prints one JSON line: tokens/s, the dominant kernel's roofline fraction
 (kernel time from HIP events the library records around that kernel, on the
@@ -47,6 +51,8 @@ CSRC = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
 WORKLOADS = {
     "decode": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=16, inputs=None,
                    sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
+    "mtp_verify": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=48, inputs=4,
+                       sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
     "prefill_2bit": dict(kernel="gemm_gateup", symbol="gemm_gateup_kernel", rotate=2, inputs=4,
                          sources=["common.hpp", "mfma.hpp", "gemm_impl.hpp", "gemm_gu2.hip"]),
 }
@@ -56,21 +62,23 @@ COPY_SYMBOL = "MulFunctor"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=None, help="timed steps (default 2000 decode, 200 prefill)")
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 2000 decode, 200 prefill, 100 verify)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (default steps / 10)")
     p.add_argument("--rotate", type=int, default=None, help="independent resident layers cycled through")
     p.add_argument("--cpu-sample-s", type=float, default=12.0, help="target seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-only", action="store_true", help="skip the CPU baseline and event pass")
     p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS),
-                   help="decode (the headline line) or the 4096-token 2-bit prefill chunk")
+                   help="decode (the headline line), the 48-layer T=5 verify step or the 4096-token 2-bit "
+                        "prefill chunk")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain fp32 elementwise copy of MIB MiB (read + write) 5 times before the warmup")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the traffic summary from two rocprofv3 counter CSVs of a --copy-calibration run")
     a = p.parse_args()
     if a.steps is None:
-        a.steps = 2000 if a.workload == "decode" else 200
+        a.steps = {"decode": 2000, "mtp_verify": 100}.get(a.workload, 200)
     if a.warmup is None:
         a.warmup = max(1, a.steps // 10)
     if a.rotate is None:
@@ -126,16 +134,22 @@ def main():
     xs = torch.from_numpy(synth.x_tokens(w, range(n_in * T), rep=1).view(np.int16)).to(dev).view(n_in, T, d)
     setup_s = time.time() - t0
 
-    ws_bytes = brx.workspace_bytes(sh, T, 1)
+    depth = w.layers                    # layers one step runs through (48 for the verify stack)
+    if nrot < depth:
+        sys.exit(f"--rotate must be at least the stack depth {depth}")
+    ws_bytes = brx.workspace_bytes(sh, T, depth)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
     resid = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     names = brx.kernel_names(sh, T)
 
-    def step(i, events=None):
-        brx.forward(sh, [layers[i % nrot]], xs[i % n_in], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
-                    events=events, stream=stream)
+    def stack(i):
+        return [layers[(i * depth + j) % nrot] for j in range(depth)]
+
+    def step(i, events=None, route_outs=None):
+        brx.forward(sh, stack(i), xs[i % n_in], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
+                    route_outs=route_outs, events=events, stream=stream)
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -161,18 +175,20 @@ def main():
     tokens_per_s = T * args.steps / (total_ms / 1e3)
 
     # ---- per-kernel durations: library-recorded HIP events around each kernel, same steps
+    # (every layer of a stack: the i-th kernel group of layer l is group l*nk + i)
     nk = len(names)
     kern_us = {n: [] for n in names}
     if not args.profile_only:
         hip = _Hip()
-        evs = [[hip.event() for _ in range(2 * nk)] for _ in range(args.steps)]
+        ev_steps = min(args.steps, max(1, 20000 // (2 * nk * depth)))
+        evs = [[hip.event() for _ in range(2 * nk * depth)] for _ in range(ev_steps)]
         torch.cuda.synchronize()
-        for j, i in enumerate(range(args.warmup, n_step)):
+        for j, i in enumerate(range(args.warmup, args.warmup + ev_steps)):
             step(i, events=evs[j])
         torch.cuda.synchronize()
-        for j in range(args.steps):
-            for q, n in enumerate(names):
-                kern_us[n].append(hip.elapsed_ms(evs[j][2 * q], evs[j][2 * q + 1]) * 1e3)
+        for j in range(ev_steps):
+            for g in range(nk * depth):
+                kern_us[names[g % nk]].append(hip.elapsed_ms(evs[j][2 * g], evs[j][2 * g + 1]) * 1e3)
         for row in evs:
             for e in row:
                 hip.destroy(e)
@@ -182,10 +198,20 @@ def main():
     dom = cfg["kernel"]
     dom_us = kern_avg.get(dom)
     roof = None
-    if args.workload == "decode":
-        # gate and up codes + scales of the 11 experts one token needs (logits
-        # and activations are a few KB and are left out)
+    if args.workload in ("decode", "mtp_verify"):
+        # gate and up codes + scales of the distinct experts the call's tokens
+        # need, plus the shared one (logits and activations are a few KB and
+        # are left out); for T > 1 the distinct count is read back from the
+        # routing of every (input batch, layer) the steps cycle through
         n_exp = k + 1
+        if T > 1:
+            uniq = []
+            for i in range(min(n_in, n_step)):
+                ro = [{"topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev)} for _ in range(depth)]
+                step(i, route_outs=ro)
+                torch.cuda.synchronize()
+                uniq += [len(np.unique(r["topk_idx"].cpu().numpy())) for r in ro]
+            n_exp = float(np.mean(uniq)) + 1
         dom_bytes = n_exp * 2 * per_mat_codes
         if dom_us:
             achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -193,9 +219,15 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": _traffic_from_profiles(args.workload), "algorithmic_bytes": dom_bytes,
                     "avg_us": round(dom_us, 3)}
-        layer_bytes_alg = n_exp * 3 * per_mat_codes + E * d * 4 + d * 2 + d * 4
-        metric = "MoE-layer tokens/s (decode T=1, full-size 3-bit layer)"
-        wl = "decode layer: E=512 top-10 + 1 shared, d=2048, f=768, 3-bit blocks, T=1"
+        layer_bytes_alg = n_exp * 3 * per_mat_codes + E * d * 4 + T * d * 2 + T * d * 4
+        if args.workload == "decode":
+            metric = "MoE-layer tokens/s (decode T=1, full-size 3-bit layer)"
+            wl = "decode layer: E=512 top-10 + 1 shared, d=2048, f=768, 3-bit blocks, T=1"
+        else:
+            metric = "MTP verify token-rows/s (T=5 through 48 full-size 3-bit layers)"
+            wl = "MTP verify: T=5 through 48 layers of E=512 top-10 + 1 shared, d=2048, f=768, 3-bit blocks"
+            if roof:
+                roof["distinct_experts_per_layer"] = round(n_exp - 1, 2)
         dtype = "int4-dot/fp32"
     else:
         # useful gate+up flops of the T*k routed and T shared token-expert pairs
@@ -228,10 +260,10 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl, "tokens_per_step": T, "resident_layers_rotated": nrot,
+        "config": {"workload": wl, "tokens_per_step": T, "layers_per_step": depth, "resident_layers_rotated": nrot,
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "layer_hbm_frac": round(layer_bytes_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_hbm_frac": round(depth * layer_bytes_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {n: (round(v, 3) if v is not None else None) for n, v in kern_avg.items()},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
@@ -343,26 +375,34 @@ def traffic_summary(args):
 def _cpu_baseline(w, target_s):
     """The oracle (grouped evaluation: each needed expert dequantised once,
     then its tokens) on a bounded sample of the workload's tokens, for about
-    target_s seconds."""
+    target_s seconds.  Calls carry one token (T = 1 and the prefill chunk) or
+    the workload's T <= 8 token batch; a stack of `layers` layers costs
+    `layers` such calls per token row."""
     import oracle
     import synth
     codes = np.empty(w.experts_total * w.code_bytes_per_expert, dtype=np.uint8)
     synth.layer_codes_into(w, 0, codes.ctypes.data)
     scales = synth.layer_scales(w, 0)
     Wr = synth.router_weights(w, 0)
-    xs = synth.bf16_to_f32(synth.x_tokens(w, range(64), rep=2))
+    tc = w.tokens_per_call if w.tokens_per_call <= 8 else 1
+    xs = synth.bf16_to_f32(synth.x_tokens(w, range(64 * tc), rep=2))
     n = 0
     t0 = time.time()
     while n < 64:
-        oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, xs[n:n + 1], Wr, codes, scales,
-                         grouped=True)
+        oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, xs[n * tc:(n + 1) * tc], Wr, codes,
+                         scales, grouped=True)
         n += 1
         if time.time() - t0 >= target_s:
             break
     el = time.time() - t0
     cores = oracle._threads()
-    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} tokens, one full-size layer each (grouped oracle, {cores} threads)"}
+    rate = n * tc / el / w.layers
+    if w.layers == 1:
+        sample = f"{n * tc} tokens in {n} calls of {tc}, one full-size layer each (grouped oracle, {cores} threads)"
+    else:
+        sample = (f"{n} calls of {tc} tokens through one full-size layer (grouped oracle, {cores} threads), "
+                  f"rate divided by the {w.layers}-layer stack depth")
+    return {"value": round(rate, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample}
 
 
 if __name__ == "__main__":

@@ -21,14 +21,15 @@ thread_local LaunchEvents g_launch_events;
 namespace {
 
 constexpr size_t ALIGN = 256;
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Token counts up to this take the decode path (one work item per expert).
 constexpr int SMALL_T = 8;
 
 struct Layout {
-    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf, xa, sx,
-        ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
+    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf, hq, hsum,
+        hscl, xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -68,6 +69,9 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.xsum = take(4 * Tq * (d / 32));
     l.xscl = take(4 * Tq * ((d + 255) / 256));
     l.hf = take(4 * Sq * f);
+    l.hq = take((size_t)Sq * (f / 32) * XPLANES * 16);
+    l.hsum = take(4 * Sq * (f / 32));
+    l.hscl = take(4 * Sq * (f / 32));
     l.xa = take((size_t)2 * Tg * d * 2);
     l.sx = take(4 * Tg * (d / 128));
     l.ha = take((size_t)2 * Sg * f * 2);
@@ -118,6 +122,9 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xsum = (int32_t *)(ws + l.xsum);
     a.xscl = (float *)(ws + l.xscl);
     a.hf = (float *)(ws + l.hf);
+    a.hq = (uint32_t *)(ws + l.hq);
+    a.hsum = (int32_t *)(ws + l.hsum);
+    a.hscl = (float *)(ws + l.hscl);
     a.Y = (float *)(ws + l.Y);
     a.xa = (uint16_t *)(ws + l.xa);
     a.sx = (float *)(ws + l.sx);
@@ -200,15 +207,15 @@ const char *strata_status_str(strata_status s) {
 }
 
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max) {
-    static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
-    static const char *small4[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
+    static const char *one[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
+    static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
     static const char *large[] = {"gemm_prep", "route_logits", "route_topk", "route_permute",
                                   "gemm_gateup", "gemm_down", "combine"};   // route_permute: three kernels
     if (check_shape(shape) != STRATA_OK) return 0;
     const bool sp = small_path(*shape, T);
-    const bool rows = sp && down_rows_fits(T, shape->top_k, shape->d_ff);
-    const char **src = sp ? (rows ? small : small4) : large;
-    const int n = sp ? (rows ? 3 : 4) : 7;
+    const bool t1 = sp && gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff);
+    const char **src = sp ? (t1 ? one : small) : large;
+    const int n = sp ? (t1 ? 3 : 4) : 7;
     for (int i = 0; i < n && i < max; ++i) names[i] = src[i];
     return n;
 }
@@ -221,6 +228,7 @@ strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_l
     if (T < 0 || !layer || (xdtype != STRATA_X_BF16 && xdtype != STRATA_X_F32)) return STRATA_EINVAL;
     if (T == 0) return STRATA_OK;
     if (!x || !layer->router_w || !ws) return STRATA_EINVAL;
+    if (!aligned16(x) || !aligned16(ws) || !aligned16(layer->router_w)) return STRATA_EINVAL;
     const Layout l = layout(*shape, T);
     if (ws_bytes < l.total) return STRATA_EWORKSPACE;
     LayerArgs a;
@@ -249,9 +257,12 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         return STRATA_EINVAL;
     if (T == 0) return STRATA_OK;
     if (!x || !y_last || !ws) return STRATA_EINVAL;
+    if (!aligned16(x) || !aligned16(y_last) || !aligned16(ws) || (resid_out && !aligned16(resid_out)))
+        return STRATA_EINVAL;
     bool any_mask = false;
     for (int l = 0; l < L; ++l) {
         if (!layers[l].router_w || !layers[l].codes || !layers[l].scales) return STRATA_EINVAL;
+        if (!aligned16(layers[l].router_w) || !aligned16(layers[l].codes)) return STRATA_EINVAL;
         any_mask |= layers[l].resident_mask != nullptr;
     }
     if (any_mask && (!miss_te || !miss_w || !miss_count)) return STRATA_EINVAL;
@@ -291,11 +302,12 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         st = route_layer(a, *shape, T, rec);
         if (st != STRATA_OK) return st;
         if (small_path(*shape, T)) {
-            RUN(launch_gemv_gateup_small(a, (int)lay.max_items, rec.s));
-            if (down_rows_fits(T, shape->top_k, shape->d_ff)) {
-                RUN(launch_gemv_down_rows(a, rec.s));
+            if (gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff)) {
+                RUN(launch_gemv_gateup_small(a, (int)lay.max_items, rec.s));
+                RUN(launch_gemv_down_one(a, rec.s));
             } else {
-                RUN(launch_gemv_down(a, (int)lay.max_items, rec.s));
+                RUN(launch_gemv_gateup_multi(a, (int)lay.max_items, rec.s));
+                RUN(launch_gemv_down_multi(a, (int)lay.max_items, rec.s));
                 RUN(launch_combine(a, rec.s));
             }
         } else {

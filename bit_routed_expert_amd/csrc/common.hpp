@@ -149,7 +149,10 @@ struct LayerArgs {
     uint32_t *xq;
     int32_t *xsum;
     float *xscl;
-    float *hf;           // [slots][f] SwiGLU activation h of each slot (decode path)
+    float *hf;           // [slots][f] SwiGLU activation h of each slot (one-token kernels)
+    uint32_t *hq;        // [slots][f/32][XPLANES][4] digit planes of h (T >= 2 kernels)
+    int32_t *hsum;       // [slots][f/32] digit sums of h
+    float *hscl;         // [slots][f/32] 2^-E of h
     float *Y;            // [slots][d] expert outputs (larger T)
     // GEMM path: bf16 hi/lo activations, columns permuted inside each
     // 128-column step, and their sums over each step (x) or 32-feature group (h)
@@ -184,13 +187,14 @@ extern thread_local LaunchEvents g_launch_events;
 hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_gemv_gateup_multi(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s);
 int route_perm_blocks(int T);
-hipError_t launch_gemv_down(const LayerArgs &a, int max_items, hipStream_t s);
-hipError_t launch_gemv_down_rows(const LayerArgs &a, hipStream_t s);
-bool down_rows_fits(int T, int k, int f);
+hipError_t launch_gemv_down_multi(const LayerArgs &a, int max_items, hipStream_t s);
+hipError_t launch_gemv_down_one(const LayerArgs &a, hipStream_t s);
+bool gemv_one_token(int T, int E, int k, int d, int f);   // T = 1 kernels apply
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemm_prep(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemm_gateup(const LayerArgs &a, int max_items, hipStream_t s);

@@ -3,6 +3,6 @@
 #include "gemv_impl.hpp"
 
 namespace strata {
-template hipError_t down_launch<3>(const LayerArgs &, int, hipStream_t);
-template hipError_t down_rows_launch<3>(const LayerArgs &, hipStream_t);
+template hipError_t down_multi_launch<3>(const LayerArgs &, int, hipStream_t);
+template hipError_t down_one_launch<3>(const LayerArgs &, hipStream_t);
 }  // namespace strata

@@ -4,4 +4,5 @@
 
 namespace strata {
 template hipError_t gateup_small_launch<3>(const LayerArgs &, int, hipStream_t);
+template hipError_t gateup_multi_launch<3>(const LayerArgs &, int, int, hipStream_t);
 }  // namespace strata

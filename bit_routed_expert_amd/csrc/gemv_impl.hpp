@@ -85,9 +85,9 @@ __device__ __forceinline__ int dig_off(int U, int units_per_slice) {
 // aligned runs of 4 units are 128-column groups, read with 16-byte loads),
 // and each unit's fp16 block scale.
 constexpr int UPL_MAX = 8;
-template <int BITS> struct UTile {
-    uint32_t w[UPL_MAX][Fmt<BITS>::UB / 4];
-    uint32_t sc[UPL_MAX];
+template <int BITS, int UPLM = UPL_MAX> struct UTile {   // UPLM: capacity (upl <= UPLM)
+    uint32_t w[UPLM][Fmt<BITS>::UB / 4];
+    uint32_t sc[UPLM];
 
     __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, const uint16_t *__restrict__ msc, int in,
                                          int row0, int R, int upl) {
@@ -97,7 +97,7 @@ template <int BITS> struct UTile {
         const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
         if (upl % 4 == 0) {   // aligned groups: 48 or 32 contiguous bytes each
 #pragma unroll
-            for (int gq = 0; gq < UPL_MAX / 4; ++gq) {
+            for (int gq = 0; gq < UPLM / 4; ++gq) {
                 if (4 * gq < upl) {
                     const uint4 *p = (const uint4 *)(mat + rbase + (int64_t)((U0 >> 2) + gq) * 64 * UB);
 #pragma unroll
@@ -112,7 +112,7 @@ template <int BITS> struct UTile {
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < UPL_MAX; ++u) {
+            for (int u = 0; u < UPLM; ++u) {
                 if (u < upl) {
                     const int U = U0 + u;
                     const uint32_t *p = (const uint32_t *)(mat + rbase + ((int64_t)(U >> 2) * 64 + (U & 3)) * UB);
@@ -122,22 +122,59 @@ template <int BITS> struct UTile {
             }
         }
 #pragma unroll
-        for (int u = 0; u < UPL_MAX; ++u)
+        for (int u = 0; u < UPLM; ++u)
             if (u < upl) sc[u] = msc[((int64_t)r * in + 32 * (U0 + u)) >> 8];
     }
 };
 
+// A UTile filled with every load issued unconditionally (units past upl
+// re-read the lane's first unit, from cache), so filling it takes no
+// branches and a prefetch into it needs no wait until its values are read.
+// GROUPED: upl is a multiple of 4 (16-byte group loads).
+template <int BITS, bool GROUPED, int UPLM = UPL_MAX>
+__device__ __forceinline__ void utile_load_all(UTile<BITS, UPLM> &t, const uint8_t *__restrict__ mat,
+                                               const uint16_t *__restrict__ msc, int in, int row0, int R, int upl) {
+    const int lane = threadIdx.x & 63;
+    const int r = row0 + lane % R, U0 = (lane / R) * upl;
+    constexpr int UB = Fmt<BITS>::UB;
+    const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int gq = 0; gq < UPLM / 4; ++gq) {
+            const int gg = 4 * gq < upl ? gq : 0;
+            const uint4 *p = (const uint4 *)(mat + rbase + (int64_t)((U0 >> 2) + gg) * 64 * UB);
+#pragma unroll
+            for (int i = 0; i < UB / 4; ++i) {
+                const uint4 v = p[i];
+                const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) t.w[4 * gq + (4 * i + c) / (UB / 4)][(4 * i + c) % (UB / 4)] = q[c];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < UPLM; ++u) {
+            const int U = U0 + (u < upl ? u : 0);
+            const uint32_t *p = (const uint32_t *)(mat + rbase + ((int64_t)(U >> 2) * 64 + (U & 3)) * UB);
+#pragma unroll
+            for (int i = 0; i < UB / 4; ++i) t.w[u][i] = p[i];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UPLM; ++u) t.sc[u] = msc[((int64_t)r * in + 32 * (U0 + (u < upl ? u : 0))) >> 8];
+}
+
 // Row sums of a UTile against NT tokens (digit planes in LDS at dig +
-// tmap[t]*dstride, laid out by dig_off with upl units per slice; unit sums
-// usum[tmap[t]*ustride + U]; activation scales gscl[tmap[t]*gstride + U/upg]).
+// tok_of(tpk, t)*dstride, laid out by dig_off with upl units per slice; unit sums
+// usum[tt*ustride + U]; activation scales gscl[tt*gstride + U/upg]; tt = tok_of(tpk, t)).
 // Partial sums are flushed into res every `period` units (a period never
 // spans two weight blocks or two activation groups) and at the slice end.
 // res[t] is complete in lanes with s == 0 (lane < R).
-template <int BITS, int NT>
-__device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int upl, int period,
+template <int BITS, int NT, int UPLM = UPL_MAX>
+__device__ __forceinline__ void utile_compute(const UTile<BITS, UPLM> &wt, int R, int upl, int period,
                                               const uint32_t *__restrict__ dig, int dstride,
                                               const int *__restrict__ usum, int ustride, const float *__restrict__ gscl,
-                                              int gstride, int upg, const int *tmap, float res[NT]) {
+                                              int gstride, int upg, uint32_t tpk, float res[NT]) {
     const int lane = threadIdx.x & 63;
     const int U0 = (lane / R) * upl;
     int acc[NT][XPLANES];
@@ -150,7 +187,7 @@ __device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int 
         for (int p = 0; p < XPLANES; ++p) acc[t][p] = 0;
     }
 #pragma unroll
-    for (int u = 0; u < UPL_MAX; ++u) {
+    for (int u = 0; u < UPLM; ++u) {
         if (u < upl) {
             const int U = U0 + u;
             uint32_t N[4];
@@ -158,7 +195,7 @@ __device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int 
             const int off = dig_off(U, upl);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const int tt = tmap ? tmap[t] : t;
+                const int tt = tok_of(tpk, t);
                 const uint4 *dp = (const uint4 *)(dig + tt * dstride + off);
 #pragma unroll
                 for (int p = 0; p < XPLANES; ++p) {
@@ -176,7 +213,7 @@ __device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int 
                 const float scl = 0.5f * half_to_float((uint16_t)wt.sc[u]);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int tt = tmap ? tmap[t] : t;
+                    const int tt = tok_of(tpk, t);
                     const float v = digits_value(acc[t], Fmt<BITS>::C2, sx[t]);
                     res[t] = fmaf(v, scl * gscl[tt * gstride + U / upg], res[t]);
                     sx[t] = 0;
@@ -189,6 +226,24 @@ __device__ __forceinline__ void utile_compute(const UTile<BITS> &wt, int R, int 
     for (int o = R; o < 64; o <<= 1) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) res[t] += __shfl_xor(res[t], o, WAVE);
+    }
+}
+
+// utile_compute over the NT tokens one at a time (each token's result is
+// the same as in a joint pass; the register footprint is that of one token,
+// so kernels holding two code tiles keep every token count spill-free).
+template <int BITS, int NT, int UPLM = UPL_MAX>
+__device__ __forceinline__ void utile_compute_each(const UTile<BITS, UPLM> &wt, int R, int upl, int period,
+                                                   const uint32_t *__restrict__ dig, int dstride,
+                                                   const int *__restrict__ usum, int ustride,
+                                                   const float *__restrict__ gscl, int gstride, int upg,
+                                                   uint32_t tpk, float res[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float r[1];
+        utile_compute<BITS, 1, UPLM>(wt, R, upl, period, dig, dstride, usum, ustride, gscl, gstride, upg,
+                                     tpk >> (3 * t), r);
+        res[t] = r[0];
     }
 }
 
@@ -272,11 +327,11 @@ __device__ __forceinline__ void xstage_issue(const LayerArgs &a, const GuLds &g,
         if (c < chunks) __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
 }
-// Gate/up for the NT tokens toks[] of one work item: waves [0, G) take gate
+// Gate/up for the NT tokens (token map tpk) of one work item: waves [0, G) take gate
 // rows j0 + R*w .. +R, waves [G, 2G) the same rows of up; then h = silu(g)
 // * u (fp32) of those G*R columns goes to hf.
 template <int BITS, int NT>
-__device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &it, const int *toks, int R,
+__device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &it, uint32_t tpk, int R,
                                             int j0, const GuLds &g) {
     const int th = threadIdx.x, wave = th >> 6, lane = th & 63, G = blockDim.x >> 7;
     const int d = a.d, f = a.f;
@@ -291,7 +346,7 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     __syncthreads();                                  // every wave's staged digit planes visible
     float res[NT];
     utile_compute<BITS, NT>(wt, R, upl, unit_period(d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl, g.G,
-                            XGROUP_UNITS, toks, res);
+                            XGROUP_UNITS, tpk, res);
     if (m == 1 && lane < R) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) g.gu[j * G * R + (wave - G) * R + lane] = res[j];
@@ -319,11 +374,10 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
         default: break;                                               \
     }
 
-// T <= 8: every block (2G waves, G*R columns of h; G = 1 for one token, 4
-// otherwise so the tokens' top-k run on separate waves) takes the top-k of
-// the T tokens itself from the router logits (a few KB) while its input
-// digit planes, unit sums and group scales load, derives its own work item
-// and runs it; the last block writes the routing outputs and the work list
+// One token (NTMAX = 1): every block (2 waves, R columns of h) takes the
+// top-k itself from the router logits (a few KB) while its input digit
+// planes, unit sums and group scales load, derives its own work item and
+// runs it; the last block writes the routing outputs and the work list
 // instead.
 template <int BITS, int NTMAX>
 __global__ __launch_bounds__(NTMAX == 1 ? 128 : 512) void gemv_gateup_small_kernel(LayerArgs a, int R,
@@ -362,12 +416,163 @@ __global__ __launch_bounds__(NTMAX == 1 ? 128 : 512) void gemv_gateup_small_kern
     }
     const int cols = (blockDim.x >> 7) * R, wg_per_item = a.f / cols;
     WorkItem it;
-    int toks[CHUNK_TOK];
-    if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, toks)) return;
+    uint32_t tpk;
+    if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, tpk)) return;
     const int j0 = (blockIdx.x % wg_per_item) * cols;
-#define GU(n) gateup_body<BITS, n>(a, it, toks, R, j0, g)
+#define GU(n) gateup_body<BITS, n>(a, it, tpk, R, j0, g)
     NT_SWITCH(GU)
 #undef GU
+}
+
+// Any T <= 8 (the path for T >= 2): each block holds 32/R gate waves and
+// as many up waves, so it covers one 32-column unit of h.  Blocks take the
+// top-k of all T tokens once (from the router logits, while every token's
+// input digit planes load into LDS), list the work items in LDS, then run
+// jobs (work item, unit of h)
+// job = blockIdx.x, + gridDim.x - 1, ..., each job's codes loading while
+// the previous one computes.  h of a job is quantised in the block exactly
+// as the one-token down kernel quantises it (per 32-column unit: exponent
+// from the unit's max |h|, 6 balanced base-16 digit planes, digit sum and
+// 2^-E) and written once for the down kernel: hq [slot][unit][plane][4
+// words], hsum / hscl [slot][unit].  The last block writes the routing
+// outputs and the work list instead.
+template <int BITS, int NT>
+__device__ __forceinline__ void gateup_multi_job(const LayerArgs &a, const WorkItem &it, uint32_t tpk, int R,
+                                                 int unit, const GuLds &g, float *hb, const UTile<BITS> &wt) {
+    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, G = blockDim.x >> 7;
+    const int upl = (a.d / 32) / (64 / R), units_h = a.f / 32;
+    const int m = wave / G, c = (wave % G) * R + lane;   // c: column of h inside the unit
+    float res[NT];
+    utile_compute_each<BITS, NT>(wt, R, upl, unit_period(a.d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl,
+                                 g.G, XGROUP_UNITS, tpk, res);
+    if (m == 1 && lane < R) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) g.gu[j * 32 + c] = res[j];
+    }
+    __syncthreads();
+    if (m == 0 && lane < R) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const float gv = res[j], u = g.gu[j * 32 + c];
+            hb[j * 32 + c] = gv / (1.f + expf(-gv)) * u;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {   // lane 4j + q: 8-column chunk q of slot j's unit
+        const int j = lane >> 2, q = lane & 3, jj = j < NT ? j : NT - 1;
+        float h[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) h[n] = hb[jj * 32 + 8 * q + n];
+        float mx = 0.f;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
+        mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+        const int E = fixed_point_exponent<XPLANES>(mx);
+        uint32_t word[XPLANES];
+        int sx = chunk_digits(h, E, word);
+        sx += __shfl_xor(sx, 1, WAVE);
+        sx += __shfl_xor(sx, 2, WAVE);
+        if (j < NT) {
+            const size_t su = (size_t)(it.slot0 + j) * units_h + unit;
+            uint32_t *dst = a.hq + su * (XPLANES * 4);
+#pragma unroll
+            for (int p = 0; p < XPLANES; ++p) dst[4 * p + q] = word[p];
+            if (q == 0) {
+                a.hsum[su] = sx;
+                a.hscl[su] = ldexpf(1.f, -E);
+            }
+        }
+    }
+}
+
+template <int BITS, int NTMAX, bool GROUPED>
+__global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int R, int route_off) {
+    extern __shared__ uint32_t lds[];
+    const GuLds g(lds, a.d, R, a.T, NTMAX);
+    float *hb = g.gu + NTMAX * 32;   // [NTMAX][32] h of the current job
+    const SmallRoute L(lds + route_off, a.E);
+    const int S = 64 / R, upl = (a.d / 32) / S;
+    if (blockIdx.x == gridDim.x - 1) {
+        small_route_compute(a, L, a.z, a.inv_rms);
+        small_route_write(a, L);
+        return;
+    }
+    xstage_issue(a, g, S, upl);
+    // unit sums and group scales into registers now, LDS after the routing
+    const int per = g.units + g.G, nq = a.T * per;
+    int qv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
+        qv[u] = q < nq ? (i < g.units ? a.xsum[(size_t)j * g.units + i] : __float_as_int(a.xscl[(size_t)j * g.G + i - g.units])) : 0;
+    }
+    small_route_compute(a, L, a.z, a.inv_rms);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
+        if (q < nq) {
+            if (i < g.units) g.sum[j * g.units + i] = qv[u];
+            else g.scl[j * g.G + i - g.units] = __int_as_float(qv[u]);
+        }
+    }
+    for (int q = threadIdx.x + 2 * blockDim.x; q < nq; q += blockDim.x) {   // large d
+        const int j = q / per, i = q % per;
+        if (i < g.units) g.sum[j * g.units + i] = a.xsum[(size_t)j * g.units + i];
+        else g.scl[j * g.G + i - g.units] = a.xscl[(size_t)j * g.G + i - g.units];
+    }
+    // every wave's staged digit planes have landed (visible after the
+    // table's barrier)
+    __builtin_amdgcn_s_waitcnt(0);
+    int32_t *itab = (int32_t *)(lds + ((route_off + small_route_lds_words(a.E) + 3) & ~3));   // 16-byte aligned
+    const int tiles = a.f / 32, nb = gridDim.x - 1;
+    const int njobs = small_route_table(a, L, itab) * tiles;
+    int job = blockIdx.x;
+    if (job >= njobs) return;
+    const int G = blockDim.x >> 7, wave = threadIdx.x >> 6;
+    const int m = wave / G, rsub = (wave % G) * R;
+    const size_t mat_bytes = (size_t)a.d * a.f * BITS / 8, mat_blocks = (size_t)a.d * a.f / 256;
+    WorkItem it;
+    uint32_t tpk;
+    {
+        const int4 v = *(const int4 *)(itab + 4 * (job / tiles));
+        it = WorkItem{v.x, v.y, v.z};
+        tpk = (uint32_t)v.w;
+    }
+    // two tiles used alternately (named, no copies): one computes while
+    // the next job's codes load into the other
+    UTile<BITS> b0, b1;
+    utile_load_all<BITS, GROUPED>(b0, a.codes + ((size_t)it.expert * 3 + m) * mat_bytes,
+                                  a.scales + ((size_t)it.expert * 3 + m) * mat_blocks, a.d, (job % tiles) * 32 + rsub,
+                                  R, upl);
+#define GU_STEP(CUR, NXT)                                                                                              \
+    {                                                                                                                  \
+        const int next = job + nb;                                                                                     \
+        const bool has = next < njobs; /* block-uniform */                                                             \
+        WorkItem it1 = it;                                                                                             \
+        const int4 v1 = *(const int4 *)(itab + 4 * ((has ? next : job) / tiles));                                     \
+        it1 = WorkItem{v1.x, v1.y, v1.z};                                                                              \
+        const uint32_t tpk1 = (uint32_t)v1.w;                                                                          \
+        const int nj = has ? next : job;   /* past the end: re-read this job's tile (cached) */                        \
+        utile_load_all<BITS, GROUPED>(NXT, a.codes + ((size_t)it1.expert * 3 + m) * mat_bytes,                        \
+                                      a.scales + ((size_t)it1.expert * 3 + m) * mat_blocks, a.d,                       \
+                                      (nj % tiles) * 32 + rsub, R, upl);                                               \
+        const int unit = job % tiles;                                                                                  \
+        NT_SWITCH(GJ_##CUR)                                                                                            \
+        if (!has) break;                                                                                               \
+        job = next;                                                                                                    \
+        it = it1;                                                                                                      \
+        tpk = tpk1;                                                                                                    \
+    }
+#define GJ_b0(n) gateup_multi_job<BITS, n>(a, it, tpk, R, unit, g, hb, b0)
+#define GJ_b1(n) gateup_multi_job<BITS, n>(a, it, tpk, R, unit, g, hb, b1)
+    for (;;) {
+        GU_STEP(b0, b1)
+        GU_STEP(b1, b0)
+    }
+#undef GJ_b0
+#undef GJ_b1
+#undef GU_STEP
 }
 
 // ----------------------------------------------------------------- down
@@ -430,101 +635,6 @@ template <int NT> struct HStage {
     }
 };
 
-__host__ __device__ inline int down_wave_lds_words(int f, int R, int nt) {
-    const int S = 64 / R;
-    return nt * ((f / 32) * XPLANES * 4 + S * 4) + 2 * nt * (f / 32);
-}
-
-// One work item on this wave's tile: stage h (its loads issued before the
-// prefetch of the next tile's codes, so waiting for them does not wait for
-// the prefetch), then run the tile.
-template <int BITS, int NT>
-__device__ __forceinline__ void down_item(const LayerArgs &a, const WorkItem &it, const UTile<BITS> &wt, int R,
-                                          int row0, uint32_t *wdig, float res[CHUNK_TOK], UTile<BITS> &next,
-                                          bool do_next, int next_expert) {
-    const int d = a.d, f = a.f, units = f / 32;
-    const int S = 64 / R, upl = units / S;
-    const int dstride = units * XPLANES * 4 + S * 4;
-    int *wsum = (int *)(wdig + NT * dstride);
-    float *wscl = (float *)(wsum + NT * units);
-    HStage<NT> st;
-    st.load(a, it.slot0);
-    if (do_next)
-        next.load(a.codes + ((size_t)next_expert * 3 + 2) * ((size_t)d * f * BITS / 8),
-                  a.scales + ((size_t)next_expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
-    st.store(a, upl, dstride, wdig, wsum, wscl);
-    float r[NT];
-    utile_compute<BITS, NT>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, nullptr, r);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) res[j] = r[j];
-}
-
-// T <= 8: block = NW waves on rows [row0, row0+R) of Wd for every work item;
-// wave w runs items w, w+NW, ... (the next item's codes are loaded while the
-// current one computes; with NW >= the number of items every wave has at
-// most one, so all codes are requested at once), expert outputs land in
-// LDS, then the block forms out[t] = y_shared[t] + sum_{r asc, resident}
-// gate[t][r] * y[slot(t, r)] and x_next = x + out for those rows.
-template <int BITS, int NTMAX>
-__global__ __launch_bounds__(256) void gemv_down_rows_kernel(LayerArgs a, int R) {
-    extern __shared__ uint32_t lds[];
-    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, NW = blockDim.x >> 6;
-    const int d = a.d, f = a.f, T = a.T, k = a.k;
-    const int row0 = blockIdx.x * R;
-    const int nslots = T * k + T;
-    float *ybuf = (float *)lds;  // [nslots][R]
-    uint32_t *wdig = lds + nslots * R + wave * down_wave_lds_words(f, R, NTMAX);
-    const int n = *a.n_items;
-    const size_t mat_bytes = (size_t)d * f * BITS / 8;
-    const size_t mat_blocks = (size_t)d * f / 256;
-    // two register tiles used alternately (named, so no dynamic register
-    // indexing); item `item` computes from one while item + NW's codes load into the other
-    UTile<BITS> buf0, buf1;
-    WorkItem cur = a.items[min(wave, n - 1)];
-    if (wave < n)
-        buf0.load(a.codes + ((size_t)cur.expert * 3 + 2) * mat_bytes,
-                  a.scales + ((size_t)cur.expert * 3 + 2) * mat_blocks, f, row0, R, (f / 32) / (64 / R));
-    for (int item = wave; item < n; item += 2 * NW) {
-        {
-            const WorkItem it = cur;
-            const bool has = item + NW < n;
-            if (has) cur = a.items[item + NW];
-            float res[CHUNK_TOK];
-#define DN(nn) down_item<BITS, nn>(a, it, buf0, R, row0, wdig, res, buf1, has, cur.expert)
-            NT_SWITCH(DN)
-#undef DN
-            if (lane < R)
-                for (int j = 0; j < it.ntok; ++j) ybuf[(it.slot0 + j) * R + lane] = res[j];
-        }
-        if (item + NW < n) {
-            const WorkItem it = cur;
-            const bool has = item + 2 * NW < n;
-            if (has) cur = a.items[item + 2 * NW];
-            float res[CHUNK_TOK];
-#define DN(nn) down_item<BITS, nn>(a, it, buf1, R, row0, wdig, res, buf0, has, cur.expert)
-            NT_SWITCH(DN)
-#undef DN
-            if (lane < R)
-                for (int j = 0; j < it.ntok; ++j) ybuf[(it.slot0 + j) * R + lane] = res[j];
-        }
-    }
-    __syncthreads();
-    for (int q = th; q < T * R; q += blockDim.x) {
-        const int t = q / R, i = q % R;
-        float s = ybuf[(T * k + t) * R + i];
-        for (int r = 0; r < k; ++r) {
-            const int e = a.idx[t * k + r];
-            if (is_resident(a.mask, e)) s = fmaf(a.gate[t * k + r], ybuf[a.pos[t * k + r] * R + i], s);
-        }
-        const size_t o = (size_t)t * d + row0 + i;
-        a.out[o] = s;
-        if (a.x_next) {
-            const float xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
-            a.x_next[o] = xv + s;
-        }
-    }
-}
-
 // One token: block = one wave per work item on rows [row0, row0+R) of Wd
 // (R = 64/S, S lane slices of upl units, so every expert's rows of this
 // tile are requested at once).  With no resident mask item w is slot w (the
@@ -575,7 +685,7 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
                 a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
         st.store(a, upl, dstride, wdig, wsum, wscl);
         float res[1];
-        utile_compute<BITS, 1>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, nullptr, res);
+        utile_compute<BITS, 1>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, TOK_IDENTITY, res);
         if (lane < R) ybuf[slot * R + lane] = res[0];
     }
     if (wave == 0 && lane < k) {
@@ -597,36 +707,94 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
     }
 }
 
-// Any T: block = 2 waves = 2 row tiles of one work item; expert outputs to Y.
-template <int BITS, int NTMAX>
-__global__ __launch_bounds__(128) void gemv_down_items_kernel(LayerArgs a, int R) {
+// Any T <= 8 (the path for T >= 2): block = one work item x 128 rows of
+// Wd (4 waves, Q = 32/R tiles of R rows each, every tile's codes requested
+// at once); the item's pre-quantised h digit planes, sums and scales are
+// copied into LDS and shared by the waves; expert outputs go to Y and the
+// combine kernel sums them.  Per (slot, row) the arithmetic is the
+// one-token kernel's, so results do not depend on T.
+constexpr int DN_WAVES = 4, DN_QMAX = 4;   // Q = 128 / (4 R): blocks own 128 rows
+
+__host__ __device__ inline int down_multi_lds_words(int f, int R, int nt) {
+    const int S = 64 / R, units = f / 32;
+    return nt * (units * XPLANES * 4 + S * 4) + 2 * nt * units;
+}
+
+template <int BITS, int NT, int UPLM>
+__device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkItem &it, const UTile<BITS, UPLM> *wt,
+                                                 int R,
+                                                 int Q, int row0, const uint32_t *dig, int dstride, const int *hsum,
+                                                 const float *hscl) {
+    const int lane = threadIdx.x & 63, units = a.f / 32, upl = units / (64 / R);
+#pragma unroll
+    for (int q = 0; q < DN_QMAX; ++q) {
+        if (q >= Q) break;
+        float res[NT];
+        utile_compute_each<BITS, NT, UPLM>(wt[q], R, upl, 1, dig, dstride, hsum, units, hscl, units, HGROUP_UNITS,
+                                           TOK_IDENTITY, res);
+        if (lane < R) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) a.Y[(size_t)(it.slot0 + j) * a.d + row0 + q * R + lane] = res[j];
+        }
+    }
+}
+
+template <int BITS, int NTMAX, int UPLM>
+__global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R, int Q) {
     extern __shared__ uint32_t lds[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int d = a.d, f = a.f;
-    const int wg_per_item = d / (2 * R);
-    const int item = blockIdx.x / wg_per_item;
+    const int th = threadIdx.x, wave = th >> 6;
+    const int d = a.d, f = a.f, units = f / 32, S = 64 / R, upl = units / S;
+    const int rows_blk = DN_WAVES * Q * R, chunks = d / rows_blk;
+    const int item = blockIdx.x / chunks;
     if (item >= *a.n_items) return;
     const WorkItem it = a.items[item];
-    const int row0 = ((blockIdx.x % wg_per_item) * 2 + wave) * R;
-    UTile<BITS> wt;
-    wt.load(a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
-            a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, (f / 32) / (64 / R));
-    uint32_t *wdig = lds + wave * down_wave_lds_words(f, R, NTMAX);
-    float res[CHUNK_TOK];
-#define DN(nn) down_item<BITS, nn>(a, it, wt, R, row0, wdig, res, wt, false, 0)
-    NT_SWITCH(DN)
-#undef DN
-    if (lane < R)
-        for (int j = 0; j < it.ntok; ++j) a.Y[(size_t)(it.slot0 + j) * d + row0 + lane] = res[j];
+    const int row0 = (blockIdx.x % chunks) * rows_blk + wave * Q * R;
+    const size_t mi = (size_t)it.expert * 3 + 2;
+    UTile<BITS, UPLM> wt[DN_QMAX];
+#pragma unroll
+    for (int q = 0; q < DN_QMAX; ++q)
+        if (q < Q)
+            wt[q].load(a.codes + mi * ((size_t)d * f * BITS / 8), a.scales + mi * ((size_t)d * f / 256), f,
+                       row0 + q * R, R, upl);
+    // the item's slots: digit planes (dig_off layout per slot), sums, scales
+    const int dstride = units * XPLANES * 4 + S * 4;
+    uint32_t *dig = lds;
+    int *hsum = (int *)(lds + NTMAX * dstride);
+    float *hscl = (float *)(hsum + NTMAX * units);
+    const int per_slot = units * XPLANES, nq = it.ntok * per_slot;
+    for (int b = 0; b < nq; b += 4 * 256) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = b + th + 256 * u;
+            v[u] = i < nq ? *(const uint4 *)(a.hq + ((size_t)it.slot0 * units) * (XPLANES * 4) + 4 * (size_t)i)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = b + th + 256 * u;
+            if (i < nq) {
+                const int j = i / per_slot, r = i % per_slot, U = r / XPLANES, p = r % XPLANES;
+                *(uint4 *)(dig + j * dstride + dig_off(U, upl) + 4 * p) = v[u];
+            }
+        }
+    }
+    for (int i = th; i < it.ntok * units; i += 256) {
+        hsum[i] = a.hsum[(size_t)it.slot0 * units + i];
+        hscl[i] = a.hscl[(size_t)it.slot0 * units + i];
+    }
+    __syncthreads();
+#define DQ(n) down_multi_tiles<BITS, n, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl)
+    NT_SWITCH(DQ)
+#undef DQ
 }
+
 
 // ------------------------------------------------------------- launchers
 inline bool gemv_supported_impl(int d, int f, int bits) {
     if (bits != 3 && bits != 2) return false;
-    if (unit_slices(d, 8) < 2 || unit_slices(f, 8) < 1) return false;   // decode tiles
+    if (unit_slices(d, 8) < 2 || unit_slices(f, 8) < 1) return false;   // decode tiles (R = 64/S in 8..32)
     if (d % 128 || f % 128 || f > 32 * MAX_HUNITS || d > 8192) return false;
-    const int Rd = 64 / unit_slices(f, 8);
-    if (d % (2 * Rd)) return false;        // down blocks own R (rows kernel) or 2R rows
     return true;
 }
 
@@ -650,52 +818,81 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
         }                                                                                            \
     } while (0)
 
+// One token: 2-wave blocks of R columns of h per work item, plus the
+// routing writer.
 template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int R = 64 / unit_slices(a.d, 8);
-    const int nt = nt_round(ntmax_for(a.T));
-    const int off = gateup_lds_words(a.d, R, a.T, nt);
+    const int off = gateup_lds_words(a.d, R, 1, 1);
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
-    const int G = (a.T == 1 || a.f % (4 * R)) ? 1 : 4;   // row groups per block
-    const dim3 grid(max_items * (a.f / (G * R)) + 1);
-    if (nt == 1 && G != 1) return hipErrorInvalidValue;
-    LAUNCH_NT(gemv_gateup_small_kernel, BITS, nt, grid, 128 * G, lds, s, a, R, off);
+    if (a.T != 1 || lds > LDS_LIMIT) return hipErrorInvalidValue;
+    STRATA_LAUNCH((gemv_gateup_small_kernel<BITS, 1>), dim3(max_items * (a.f / R) + 1), dim3(128), lds, s, a, R, off);
     return hipGetLastError();
 }
 
-template <int BITS> hipError_t down_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / unit_slices(a.f, 8);
+// T <= 8 job loop: 32/R gate + 32/R up waves per block, about 8 waves per
+// compute unit (the job body holds two code tiles and up to ~250 VGPRs),
+// plus the routing writer.
+template <int BITS> hipError_t gateup_multi_launch(const LayerArgs &a, int max_items, int cus, hipStream_t s) {
+    const int R = 64 / unit_slices(a.d, 8), G = 32 / R;
     const int nt = nt_round(ntmax_for(a.T));
-    const size_t lds = 4 * (size_t)2 * down_wave_lds_words(a.f, R, nt);
-    const dim3 grid(max_items * (a.d / (2 * R)));
-    LAUNCH_NT(gemv_down_items_kernel, BITS, nt, grid, 128, lds, s, a, R);
-    return hipGetLastError();
-}
-
-// Waves of the down rows kernels: one token, one per work item (k + 1);
-// else 4, or fewer when the LDS does not hold them.
-static inline size_t down_rows_lds(int T, int k, int f, int R, int nt, int nw) {
-    const int nslots = T * k + T;
-    return 4 * ((size_t)nslots * R + (size_t)nw * down_wave_lds_words(f, R, nt));
-}
-static inline int down_rows_waves(int T, int k, int f, int R, int nt) {
-    int nw = T == 1 ? k + 1 : 4;
-    while (nw > 1 && down_rows_lds(T, k, f, R, nt, nw) > LDS_LIMIT) --nw;
-    return nw;
-}
-
-template <int BITS> hipError_t down_rows_launch(const LayerArgs &a, hipStream_t s) {
-    const int R = 64 / unit_slices(a.f, 8);
-    const int nt = nt_round(ntmax_for(a.T));
-    const int nw = down_rows_waves(a.T, a.k, a.f, R, nt);
-    const size_t lds = down_rows_lds(a.T, a.k, a.f, R, nt, nw);
-    const dim3 grid(a.d / R);
-    if (a.T == 1) {
-        const size_t lds1 = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
-        if (lds1 > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
-        STRATA_LAUNCH(gemv_down_rows_one_kernel<BITS>, grid, dim3(64 * (a.k + 1)), lds1, s, a, R);
-        return hipGetLastError();
+    const int off = gateup_lds_words(a.d, R, a.T, nt) + nt * 32;
+    const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E) + 3 + small_route_table_words(a.T, a.k, a.E));
+    const int jobs = max_items * (a.f / 32);
+    const int grid = std::min(jobs, std::max(1, cus) * 4 / G) + 1;
+    const int upl = (a.d / 32) / (64 / R);
+    if (32 % R || lds > LDS_LIMIT) return hipErrorInvalidValue;
+    if (upl % 4 == 0) {
+        switch (nt) {
+            case 1: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 1, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 2: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 2, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 4: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 4, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 5: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 5, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            default: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 8, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+        }
+    } else {
+        switch (nt) {
+            case 1: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 1, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 2: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 2, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 4: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 4, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            case 5: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 5, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+            default: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 8, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
+        }
     }
-    LAUNCH_NT(gemv_down_rows_kernel, BITS, nt, grid, 64 * nw, lds, s, a, R);
+    return hipGetLastError();
+}
+
+template <int BITS> hipError_t down_multi_launch(const LayerArgs &a, int max_items, hipStream_t s) {
+    const int R = 64 / unit_slices(a.f, 8), Q = 128 / (DN_WAVES * R);
+    const int nt = nt_round(ntmax_for(a.T));
+    const size_t lds = 4 * (size_t)down_multi_lds_words(a.f, R, nt);
+    const int upl = (a.f / 32) / (64 / R);
+    if (Q < 1 || Q > DN_QMAX || a.d % 128 || lds > LDS_LIMIT) return hipErrorInvalidValue;
+    const dim3 grid(max_items * (a.d / 128)), block(64 * DN_WAVES);
+#define DN_LAUNCH(UPLM)                                                                                                \
+    switch (nt) {                                                                                                      \
+        case 1: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 1, UPLM>), grid, block, lds, s, a, R, Q); break;          \
+        case 2: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 2, UPLM>), grid, block, lds, s, a, R, Q); break;          \
+        case 4: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 4, UPLM>), grid, block, lds, s, a, R, Q); break;          \
+        case 5: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 5, UPLM>), grid, block, lds, s, a, R, Q); break;          \
+        default: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 8, UPLM>), grid, block, lds, s, a, R, Q); break;         \
+    }
+    if (upl == 3) {   // d_ff = 768: 3 units per lane
+        DN_LAUNCH(3)
+    } else if (upl == 1) {
+        DN_LAUNCH(1)
+    } else {
+        DN_LAUNCH(UPL_MAX)
+    }
+#undef DN_LAUNCH
+    return hipGetLastError();
+}
+
+// One token: block = one wave per work item (k + 1 of them) on R rows.
+template <int BITS> hipError_t down_one_launch(const LayerArgs &a, hipStream_t s) {
+    const int R = 64 / unit_slices(a.f, 8);
+    const size_t lds = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
+    if (a.T != 1 || lds > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
+    STRATA_LAUNCH(gemv_down_rows_one_kernel<BITS>, dim3(a.d / R), dim3(64 * (a.k + 1)), lds, s, a, R);
     return hipGetLastError();
 }
 

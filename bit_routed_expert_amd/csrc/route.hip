@@ -114,8 +114,34 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
             wv[j] = (e < E && i < d) ? *(const float4 *)(wrow + i) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if (c0 == 0) {
-            for (int i = th; i < T * d; i += 256)
-                xs[i] = XBF16 ? bf16_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
+            // the T rows of x into LDS as fp32: 16-byte loads, eight per thread in flight
+            constexpr int PER = XBF16 ? 8 : 4;   // values per 16-byte chunk
+            const int nch = T * d / PER;
+            for (int b = 0; b < nch; b += 8 * 256) {
+                uint4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int c = b + th + 256 * j;
+                    v[j] = c < nch ? ((const uint4 *)a.x)[c] : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int c = b + th + 256 * j;
+                    if (c < nch) {
+                        const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                        if (XBF16) {
+                            float4 *dst = (float4 *)(xs + 8 * c);
+                            dst[0] = make_float4(__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xFFFF0000u),
+                                                 __uint_as_float(q[1] << 16), __uint_as_float(q[1] & 0xFFFF0000u));
+                            dst[1] = make_float4(__uint_as_float(q[2] << 16), __uint_as_float(q[2] & 0xFFFF0000u),
+                                                 __uint_as_float(q[3] << 16), __uint_as_float(q[3] & 0xFFFF0000u));
+                        } else {
+                            *(float4 *)(xs + 4 * c) = make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]),
+                                                                  __uint_as_float(q[2]), __uint_as_float(q[3]));
+                        }
+                    }
+                }
+            }
             __syncthreads();
         }
 #pragma unroll

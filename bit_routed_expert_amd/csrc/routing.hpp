@@ -196,13 +196,18 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
     __syncthreads();
 }
 
+// Token of slot j of a work item from its packed token map: 3 bits per
+// slot (tokens < 8), slot j in bits [3j, 3j+3).
+constexpr uint32_t TOK_IDENTITY = 0xFAC688u;   // slot j -> token j
+__host__ __device__ __forceinline__ int tok_of(uint32_t tpk, int j) { return (int)((tpk >> (3 * j)) & 7u); }
+
 // Work item `item` of this routing, computed by every wave alike (no block
 // barrier): the item-th picked resident expert in ascending order, or, for
 // item == their number, the shared expert with all T tokens.  Slots of
 // expert e start at the number of picks of experts below e.  Returns false
-// past the last item.  toks[j] = token of slot j.
+// past the last item.  tpk: packed token map (token of slot j = tok_of(tpk, j)).
 __device__ __forceinline__ bool small_route_item(const LayerArgs &a, const SmallRoute &L, int item, WorkItem &it,
-                                                 int *toks) {
+                                                 uint32_t &tpk) {
     const int lane = threadIdx.x & 63, n = a.T * a.k;
     const int c = lane < 32 ? __popc(L.picked[lane]) : 0;
     int pre = c;   // inclusive prefix of the bitmap word counts
@@ -215,8 +220,7 @@ __device__ __forceinline__ bool small_route_item(const LayerArgs &a, const Small
     if (item > nres) return false;
     if (item == nres) {
         it = WorkItem{a.E, n, a.T};
-#pragma unroll
-        for (int j = 0; j < CHUNK_TOK; ++j) toks[j] = j;
+        tpk = TOK_IDENTITY;
         return true;
     }
     const int w = __ffsll((unsigned long long)__ballot(lane < 32 && pre > item)) - 1;
@@ -230,13 +234,57 @@ __device__ __forceinline__ bool small_route_item(const LayerArgs &a, const Small
     }
     const uint32_t mk = (uint32_t)L.tokmask[e];
     it = WorkItem{e, below, (int32_t)__popc(mk)};
-    uint32_t rest = mk;   // toks[j]: the j-th set bit (fixed indices keep toks in registers)
+    uint32_t rest = mk;   // slot j: the j-th set bit of the token mask
+    tpk = 0;
 #pragma unroll
     for (int j = 0; j < CHUNK_TOK; ++j) {
-        toks[j] = rest ? __ffs(rest) - 1 : 0;
+        tpk |= (uint32_t)(rest ? __ffs(rest) - 1 : 0) << (3 * j);
         rest &= rest - 1u;
     }
     return true;
+}
+
+// Every work item of this routing, in small_route_item's order, into LDS
+// (whole block): itab[4i .. 4i+3] = expert, first slot, token count, packed
+// token map.  Returns the number of items.  small_route_table_words(T, k, E)
+// words of itab.
+__host__ __device__ constexpr int small_route_table_words(int T, int k, int E) {
+    return 4 * ((T * k < E ? T * k : E) + 1);
+}
+__device__ __forceinline__ int small_route_table(const LayerArgs &a, const SmallRoute &L, int32_t *itab) {
+    const int th = threadIdx.x, nth = blockDim.x;
+    const int E = a.E, T = a.T, n = T * a.k;
+    const int ept = (E + nth - 1) / nth;
+    int c_loc = 0, a_loc = 0;
+    for (int j = 0; j < ept; ++j) {
+        const int e = th * ept + j;
+        if (e < E) {
+            c_loc += __popc((uint32_t)L.tokmask[e]);
+            a_loc += (L.picked[e >> 5] >> (e & 31)) & 1u;
+        }
+    }
+    int tot;
+    const int ex = block_excl_scan((a_loc << 16) | c_loc, L.tmp, &tot);
+    int off = ex & 0xFFFF, ai = ex >> 16;
+    for (int j = 0; j < ept; ++j) {
+        const int e = th * ept + j;
+        if (e < E) {
+            const uint32_t mk = (uint32_t)L.tokmask[e];
+            if ((L.picked[e >> 5] >> (e & 31)) & 1u) {
+                uint32_t rest = mk, tpk = 0;
+                for (int q = 0; rest; ++q) {
+                    tpk |= (uint32_t)(__ffs(rest) - 1) << (3 * q);
+                    rest &= rest - 1u;
+                }
+                *(int4 *)(itab + 4 * ai) = make_int4(e, off, __popc(mk), (int)tpk);
+                ++ai;
+            }
+            off += __popc(mk);
+        }
+    }
+    if (th == 0) *(int4 *)(itab + 4 * (tot >> 16)) = make_int4(E, n, T, (int)TOK_IDENTITY);
+    __syncthreads();
+    return (tot >> 16) + 1;
 }
 
 // One block: write the routing outputs (ids, gates, counts, offsets,

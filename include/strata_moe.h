@@ -55,6 +55,9 @@
  *   race.
  *   The workspace must be zero-filled before its first use; every call
  *   leaves its internal counters at zero again.
+ *   x, y_last, resid_out, the workspace, router weights and codes must be
+ *   16-byte aligned (hipMalloc and torch allocations are); a misaligned one
+ *   is rejected with STRATA_EINVAL.
  */
 #ifndef STRATA_MOE_H
 #define STRATA_MOE_H
