@@ -28,8 +28,8 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr int SMALL_T = 8;
 
 struct Layout {
-    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf, hq, hsum,
-        hscl, xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
+    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf,
+        xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -37,10 +37,11 @@ bool small_path(const strata_moe_shape &s, int64_t T) {
     return T <= SMALL_T && (size_t)T * s.d_model * sizeof(float) <= 64 * 1024;
 }
 
-// Work items: one per picked expert (decode path), else tiles of up to
-// GEMM_BM tokens per resident expert with picks plus the shared expert's.
+// Work items: an expert's slots in pairs (decode path: at most one per
+// pick, plus the shared expert's), else tiles of up to GEMM_BM tokens per
+// resident expert with picks plus the shared expert's.
 int64_t max_items_for(const strata_moe_shape &s, int64_t T) {
-    if (small_path(s, T)) return std::min<int64_t>(s.n_experts, T * s.top_k) + 1;
+    if (small_path(s, T)) return T * s.top_k + (T + ITEM_TOK - 1) / ITEM_TOK;
     return (T * s.top_k + GEMM_BM - 1) / GEMM_BM + s.n_experts + (T + GEMM_BM - 1) / GEMM_BM + 2;
 }
 
@@ -69,9 +70,6 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.xsum = take(4 * Tq * (d / 32));
     l.xscl = take(4 * Tq * ((d + 255) / 256));
     l.hf = take(4 * Sq * f);
-    l.hq = take((size_t)Sq * (f / 32) * XPLANES * 16);
-    l.hsum = take(4 * Sq * (f / 32));
-    l.hscl = take(4 * Sq * (f / 32));
     l.xa = take((size_t)2 * Tg * d * 2);
     l.sx = take(4 * Tg * (d / 128));
     l.ha = take((size_t)2 * Sg * f * 2);
@@ -122,9 +120,6 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xsum = (int32_t *)(ws + l.xsum);
     a.xscl = (float *)(ws + l.xscl);
     a.hf = (float *)(ws + l.hf);
-    a.hq = (uint32_t *)(ws + l.hq);
-    a.hsum = (int32_t *)(ws + l.hsum);
-    a.hscl = (float *)(ws + l.hscl);
     a.Y = (float *)(ws + l.Y);
     a.xa = (uint16_t *)(ws + l.xa);
     a.sx = (float *)(ws + l.sx);

@@ -8,7 +8,8 @@
 namespace strata {
 
 constexpr int WAVE = 64;
-constexpr int CHUNK_TOK = 8;      // tokens one expert work item carries (GEMV path)
+constexpr int CHUNK_TOK = 8;      // most tokens a GEMV-path kernel call takes
+constexpr int ITEM_TOK = 2;       // tokens one GEMV-path work item carries (an expert's slots in pairs)
 constexpr int XPLANES = 6;        // base-16 digit planes of an activation (24-bit fixed point)
 constexpr int GEMM_BM = 96;       // tokens per expert tile (GEMM path)
 constexpr int GEMM_MAX_K = 4096;  // largest d and f the GEMM path stages
@@ -100,7 +101,8 @@ __device__ float token_inv_rms(const Args &a, int t, float *red) {
     return 1.f / sqrtf(tot / (float)d + RMS_EPS);
 }
 
-// Work item of the expert kernels: up to CHUNK_TOK tokens of one expert.
+// Work item of the expert kernels: consecutive slots of one expert (up to
+// ITEM_TOK on the GEMV path, GEMM_BM on the GEMM path).
 struct WorkItem {
     int32_t expert;     // 0..E-1 routed, E shared
     int32_t slot0;      // first slot; slots slot0 .. slot0+ntok-1
@@ -149,10 +151,7 @@ struct LayerArgs {
     uint32_t *xq;
     int32_t *xsum;
     float *xscl;
-    float *hf;           // [slots][f] SwiGLU activation h of each slot (one-token kernels)
-    uint32_t *hq;        // [slots][f/32][XPLANES][4] digit planes of h (T >= 2 kernels)
-    int32_t *hsum;       // [slots][f/32] digit sums of h
-    float *hscl;         // [slots][f/32] 2^-E of h
+    float *hf;           // [slots][f] SwiGLU activation h of each slot (GEMV path)
     float *Y;            // [slots][d] expert outputs (larger T)
     // GEMM path: bf16 hi/lo activations, columns permuted inside each
     // 128-column step, and their sums over each step (x) or 32-feature group (h)

@@ -131,11 +131,10 @@ template <int BITS, int UPLM = UPL_MAX> struct UTile {   // UPLM: capacity (upl 
 // re-read the lane's first unit, from cache), so filling it takes no
 // branches and a prefetch into it needs no wait until its values are read.
 // GROUPED: upl is a multiple of 4 (16-byte group loads).
+// r: this lane's row, U0: its first unit.
 template <int BITS, bool GROUPED, int UPLM = UPL_MAX>
 __device__ __forceinline__ void utile_load_all(UTile<BITS, UPLM> &t, const uint8_t *__restrict__ mat,
-                                               const uint16_t *__restrict__ msc, int in, int row0, int R, int upl) {
-    const int lane = threadIdx.x & 63;
-    const int r = row0 + lane % R, U0 = (lane / R) * upl;
+                                               const uint16_t *__restrict__ msc, int in, int r, int U0, int upl) {
     constexpr int UB = Fmt<BITS>::UB;
     const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
     if constexpr (GROUPED) {
@@ -361,29 +360,15 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     }
 }
 
-#define NT_SWITCH(BODY)                                               \
-    switch (it.ntok) {                                                \
-        case 1: if constexpr (1 <= NTMAX) BODY(1); break;             \
-        case 2: if constexpr (2 <= NTMAX) BODY(2); break;             \
-        case 3: if constexpr (3 <= NTMAX) BODY(3); break;             \
-        case 4: if constexpr (4 <= NTMAX) BODY(4); break;             \
-        case 5: if constexpr (5 <= NTMAX) BODY(5); break;             \
-        case 6: if constexpr (6 <= NTMAX) BODY(6); break;             \
-        case 7: if constexpr (7 <= NTMAX) BODY(7); break;             \
-        case 8: if constexpr (8 <= NTMAX) BODY(8); break;             \
-        default: break;                                               \
-    }
-
-// One token (NTMAX = 1): every block (2 waves, R columns of h) takes the
+// One token: every block (2 waves, R columns of h) takes the
 // top-k itself from the router logits (a few KB) while its input digit
 // planes, unit sums and group scales load, derives its own work item and
 // runs it; the last block writes the routing outputs and the work list
 // instead.
-template <int BITS, int NTMAX>
-__global__ __launch_bounds__(NTMAX == 1 ? 128 : 512) void gemv_gateup_small_kernel(LayerArgs a, int R,
-                                                                                   int route_off) {
+template <int BITS>
+__global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
-    const GuLds g(lds, a.d, R, a.T, NTMAX);
+    const GuLds g(lds, a.d, R, a.T, 1);
     const SmallRoute L(lds + route_off, a.E);
     const int S = 64 / R, upl = (a.d / 32) / S;
     if (blockIdx.x == gridDim.x - 1) {
@@ -419,78 +404,38 @@ __global__ __launch_bounds__(NTMAX == 1 ? 128 : 512) void gemv_gateup_small_kern
     uint32_t tpk;
     if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, tpk)) return;
     const int j0 = (blockIdx.x % wg_per_item) * cols;
-#define GU(n) gateup_body<BITS, n>(a, it, tpk, R, j0, g)
-    NT_SWITCH(GU)
-#undef GU
+    gateup_body<BITS, 1>(a, it, tpk, R, j0, g);
 }
 
-// Any T <= 8 (the path for T >= 2): each block holds 32/R gate waves and
-// as many up waves, so it covers one 32-column unit of h.  Blocks take the
-// top-k of all T tokens once (from the router logits, while every token's
-// input digit planes load into LDS), list the work items in LDS, then run
-// jobs (work item, unit of h)
-// job = blockIdx.x, + gridDim.x - 1, ..., each job's codes loading while
-// the previous one computes.  h of a job is quantised in the block exactly
-// as the one-token down kernel quantises it (per 32-column unit: exponent
-// from the unit's max |h|, 6 balanced base-16 digit planes, digit sum and
-// 2^-E) and written once for the down kernel: hq [slot][unit][plane][4
-// words], hsum / hscl [slot][unit].  The last block writes the routing
-// outputs and the work list instead.
+// Any T <= 8 (the path for T >= 2).  Blocks take the top-k of all T tokens
+// once (from the router logits, while every token's input digit planes load
+// into LDS) and list the work items (an expert's slots in pairs) in LDS;
+// then every wave runs its own jobs, job = (work item, R/2 columns of h),
+// jobs wave_id, wave_id + total waves, ..., the next job's codes loading
+// into a second named tile while the current one computes.  In a job, lane
+// rows r < R/2 are gate rows and r >= R/2 the same rows of up, so h =
+// silu(g) * u forms inside the wave (no block barrier) and goes to hf; the
+// down kernel quantises it.  The last block writes the routing outputs and
+// the work list instead.
 template <int BITS, int NT>
-__device__ __forceinline__ void gateup_multi_job(const LayerArgs &a, const WorkItem &it, uint32_t tpk, int R,
-                                                 int unit, const GuLds &g, float *hb, const UTile<BITS> &wt) {
-    const int th = threadIdx.x, wave = th >> 6, lane = th & 63, G = blockDim.x >> 7;
-    const int upl = (a.d / 32) / (64 / R), units_h = a.f / 32;
-    const int m = wave / G, c = (wave % G) * R + lane;   // c: column of h inside the unit
+__device__ __forceinline__ void gateup_wave_job(const LayerArgs &a, const WorkItem &it, uint32_t tpk, int R, int c0,
+                                                const GuLds &g, const UTile<BITS> &wt) {
+    const int lane = threadIdx.x & 63, half = R / 2;
+    const int upl = (a.d / 32) / (64 / R);
     float res[NT];
     utile_compute_each<BITS, NT>(wt, R, upl, unit_period(a.d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl,
                                  g.G, XGROUP_UNITS, tpk, res);
-    if (m == 1 && lane < R) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) g.gu[j * 32 + c] = res[j];
-    }
-    __syncthreads();
-    if (m == 0 && lane < R) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const float gv = res[j], u = g.gu[j * 32 + c];
-            hb[j * 32 + c] = gv / (1.f + expf(-gv)) * u;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {   // lane 4j + q: 8-column chunk q of slot j's unit
-        const int j = lane >> 2, q = lane & 3, jj = j < NT ? j : NT - 1;
-        float h[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) h[n] = hb[jj * 32 + 8 * q + n];
-        float mx = 0.f;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
-        mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
-        const int E = fixed_point_exponent<XPLANES>(mx);
-        uint32_t word[XPLANES];
-        int sx = chunk_digits(h, E, word);
-        sx += __shfl_xor(sx, 1, WAVE);
-        sx += __shfl_xor(sx, 2, WAVE);
-        if (j < NT) {
-            const size_t su = (size_t)(it.slot0 + j) * units_h + unit;
-            uint32_t *dst = a.hq + su * (XPLANES * 4);
-#pragma unroll
-            for (int p = 0; p < XPLANES; ++p) dst[4 * p + q] = word[p];
-            if (q == 0) {
-                a.hsum[su] = sx;
-                a.hscl[su] = ldexpf(1.f, -E);
-            }
-        }
+    for (int j = 0; j < NT; ++j) {
+        const float gv = res[j], u = __shfl_down(res[j], half, WAVE);
+        if (lane < half) a.hf[(size_t)(it.slot0 + j) * a.f + c0 + lane] = gv / (1.f + expf(-gv)) * u;
     }
 }
 
-template <int BITS, int NTMAX, bool GROUPED>
+template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
-    const GuLds g(lds, a.d, R, a.T, NTMAX);
-    float *hb = g.gu + NTMAX * 32;   // [NTMAX][32] h of the current job
+    const GuLds g(lds, a.d, R, a.T, ITEM_TOK);
     const SmallRoute L(lds + route_off, a.E);
     const int S = 64 / R, upl = (a.d / 32) / S;
     if (blockIdx.x == gridDim.x - 1) {
@@ -521,58 +466,54 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
         if (i < g.units) g.sum[j * g.units + i] = a.xsum[(size_t)j * g.units + i];
         else g.scl[j * g.G + i - g.units] = a.xscl[(size_t)j * g.G + i - g.units];
     }
-    // every wave's staged digit planes have landed (visible after the
-    // table's barrier)
+    // this wave's staged digit planes have landed (every wave's are visible
+    // after the table's barrier)
     __builtin_amdgcn_s_waitcnt(0);
     int32_t *itab = (int32_t *)(lds + ((route_off + small_route_lds_words(a.E) + 3) & ~3));   // 16-byte aligned
-    const int tiles = a.f / 32, nb = gridDim.x - 1;
-    const int njobs = small_route_table(a, L, itab) * tiles;
-    int job = blockIdx.x;
+    const int half = R / 2, groups = a.f / half;
+    const int njobs = small_route_table(a, L, itab) * groups;   // last block barrier
+    const int wpb = blockDim.x >> 6, nw = (gridDim.x - 1) * wpb;
+    int job = blockIdx.x * wpb + (threadIdx.x >> 6);
     if (job >= njobs) return;
-    const int G = blockDim.x >> 7, wave = threadIdx.x >> 6;
-    const int m = wave / G, rsub = (wave % G) * R;
+    const int lane = threadIdx.x & 63, rl = lane % R, m = rl >= half ? 1 : 0, U0 = (lane / R) * upl;
     const size_t mat_bytes = (size_t)a.d * a.f * BITS / 8, mat_blocks = (size_t)a.d * a.f / 256;
+    // this lane's row of the job's expert: gate (m = 0) or up (m = 1) row c0 + rl - m*half
+#define GU_LOAD(T_, IT_, JOB_)                                                                                         \
+    utile_load_all<BITS, GROUPED>(T_, a.codes + ((size_t)(IT_).expert * 3 + m) * mat_bytes,                           \
+                                  a.scales + ((size_t)(IT_).expert * 3 + m) * mat_blocks, a.d,                         \
+                                  ((JOB_) % groups) * half + rl - m * half, U0, upl)
     WorkItem it;
     uint32_t tpk;
     {
-        const int4 v = *(const int4 *)(itab + 4 * (job / tiles));
+        const int4 v = *(const int4 *)(itab + 4 * (job / groups));
         it = WorkItem{v.x, v.y, v.z};
         tpk = (uint32_t)v.w;
     }
-    // two tiles used alternately (named, no copies): one computes while
-    // the next job's codes load into the other
+    // two tiles used alternately (named, no copies)
     UTile<BITS> b0, b1;
-    utile_load_all<BITS, GROUPED>(b0, a.codes + ((size_t)it.expert * 3 + m) * mat_bytes,
-                                  a.scales + ((size_t)it.expert * 3 + m) * mat_blocks, a.d, (job % tiles) * 32 + rsub,
-                                  R, upl);
+    GU_LOAD(b0, it, job);
 #define GU_STEP(CUR, NXT)                                                                                              \
     {                                                                                                                  \
-        const int next = job + nb;                                                                                     \
-        const bool has = next < njobs; /* block-uniform */                                                             \
-        WorkItem it1 = it;                                                                                             \
-        const int4 v1 = *(const int4 *)(itab + 4 * ((has ? next : job) / tiles));                                     \
-        it1 = WorkItem{v1.x, v1.y, v1.z};                                                                              \
-        const uint32_t tpk1 = (uint32_t)v1.w;                                                                          \
-        const int nj = has ? next : job;   /* past the end: re-read this job's tile (cached) */                        \
-        utile_load_all<BITS, GROUPED>(NXT, a.codes + ((size_t)it1.expert * 3 + m) * mat_bytes,                        \
-                                      a.scales + ((size_t)it1.expert * 3 + m) * mat_blocks, a.d,                       \
-                                      (nj % tiles) * 32 + rsub, R, upl);                                               \
-        const int unit = job % tiles;                                                                                  \
-        NT_SWITCH(GJ_##CUR)                                                                                            \
+        const int next = job + nw;                                                                                     \
+        const bool has = next < njobs;                                                                                 \
+        const int nj = has ? next : job; /* past the end: re-read this job's tile (cached) */                          \
+        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));                                                     \
+        const WorkItem it1{v1.x, v1.y, v1.z};                                                                          \
+        GU_LOAD(NXT, it1, nj);                                                                                         \
+        const int c0 = (job % groups) * half;                                                                          \
+        if (it.ntok == 1) gateup_wave_job<BITS, 1>(a, it, tpk, R, c0, g, CUR);                                         \
+        else gateup_wave_job<BITS, 2>(a, it, tpk, R, c0, g, CUR);                                                      \
         if (!has) break;                                                                                               \
         job = next;                                                                                                    \
         it = it1;                                                                                                      \
-        tpk = tpk1;                                                                                                    \
+        tpk = (uint32_t)v1.w;                                                                                          \
     }
-#define GJ_b0(n) gateup_multi_job<BITS, n>(a, it, tpk, R, unit, g, hb, b0)
-#define GJ_b1(n) gateup_multi_job<BITS, n>(a, it, tpk, R, unit, g, hb, b1)
     for (;;) {
         GU_STEP(b0, b1)
         GU_STEP(b1, b0)
     }
-#undef GJ_b0
-#undef GJ_b1
 #undef GU_STEP
+#undef GU_LOAD
 }
 
 // ----------------------------------------------------------------- down
@@ -707,24 +648,26 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
     }
 }
 
-// Any T <= 8 (the path for T >= 2): block = one work item x 128 rows of
-// Wd (4 waves, Q = 32/R tiles of R rows each, every tile's codes requested
-// at once); the item's pre-quantised h digit planes, sums and scales are
-// copied into LDS and shared by the waves; expert outputs go to Y and the
-// combine kernel sums them.  Per (slot, row) the arithmetic is the
-// one-token kernel's, so results do not depend on T.
+// Any T <= 8 (the path for T >= 2): block = one work item (<= 2 slots) x
+// 128 rows of Wd (4 waves, Q = 32/R tiles of R rows each, every tile's
+// codes requested at once).  The item's h rows are quantised into LDS
+// while the codes load, exactly as the one-token kernel quantises them
+// (per 32-column unit: exponent from the unit's max |h|, 6 balanced base-16
+// digit planes, digit sum, 2^-E; the 4 chunks of a unit in 4 neighbouring
+// lanes), and shared by the waves; expert outputs go to Y and the combine
+// kernel sums them.  Per (slot, row) the arithmetic is the one-token
+// kernel's, so results do not depend on T.
 constexpr int DN_WAVES = 4, DN_QMAX = 4;   // Q = 128 / (4 R): blocks own 128 rows
 
-__host__ __device__ inline int down_multi_lds_words(int f, int R, int nt) {
+__host__ __device__ inline int down_multi_lds_words(int f, int R) {
     const int S = 64 / R, units = f / 32;
-    return nt * (units * XPLANES * 4 + S * 4) + 2 * nt * units;
+    return ITEM_TOK * (units * XPLANES * 4 + S * 4) + 2 * ITEM_TOK * units;
 }
 
 template <int BITS, int NT, int UPLM>
 __device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkItem &it, const UTile<BITS, UPLM> *wt,
-                                                 int R,
-                                                 int Q, int row0, const uint32_t *dig, int dstride, const int *hsum,
-                                                 const float *hscl) {
+                                                 int R, int Q, int row0, const uint32_t *dig, int dstride,
+                                                 const int *hsum, const float *hscl) {
     const int lane = threadIdx.x & 63, units = a.f / 32, upl = units / (64 / R);
 #pragma unroll
     for (int q = 0; q < DN_QMAX; ++q) {
@@ -739,10 +682,10 @@ __device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkI
     }
 }
 
-template <int BITS, int NTMAX, int UPLM>
+template <int BITS, int UPLM>
 __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R, int Q) {
     extern __shared__ uint32_t lds[];
-    const int th = threadIdx.x, wave = th >> 6;
+    const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
     const int d = a.d, f = a.f, units = f / 32, S = 64 / R, upl = units / S;
     const int rows_blk = DN_WAVES * Q * R, chunks = d / rows_blk;
     const int item = blockIdx.x / chunks;
@@ -756,39 +699,43 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
         if (q < Q)
             wt[q].load(a.codes + mi * ((size_t)d * f * BITS / 8), a.scales + mi * ((size_t)d * f / 256), f,
                        row0 + q * R, R, upl);
-    // the item's slots: digit planes (dig_off layout per slot), sums, scales
     const int dstride = units * XPLANES * 4 + S * 4;
     uint32_t *dig = lds;
-    int *hsum = (int *)(lds + NTMAX * dstride);
-    float *hscl = (float *)(hsum + NTMAX * units);
-    const int per_slot = units * XPLANES, nq = it.ntok * per_slot;
-    for (int b = 0; b < nq; b += 4 * 256) {
-        uint4 v[4];
+    int *hsum = (int *)(lds + ITEM_TOK * dstride);
+    float *hscl = (float *)(hsum + ITEM_TOK * units);
+    // quantise the item's h rows: chunk c (8 columns) of slot j = c / (f/8)
+    const int cps = f / 8, nch = it.ntok * cps;
+    for (int b = 0; b < nch; b += 256) {   // uniform trip count: every lane takes part in the shuffles
+        const int c = b + th, cc = min(c, nch - 1);
+        const float4 *src = (const float4 *)(a.hf + (size_t)it.slot0 * f) + 2 * cc;
+        const float4 v0 = src[0], v1 = src[1];
+        const float h[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        float mx = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = b + th + 256 * u;
-            v[u] = i < nq ? *(const uint4 *)(a.hq + ((size_t)it.slot0 * units) * (XPLANES * 4) + 4 * (size_t)i)
-                          : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
+        mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+        const int E = fixed_point_exponent<XPLANES>(mx);
+        uint32_t word[XPLANES];
+        int sx = chunk_digits(h, E, word);
+        sx += __shfl_xor(sx, 1, WAVE);
+        sx += __shfl_xor(sx, 2, WAVE);
+        if (c < nch) {
+            const int j = c / cps, U = (c % cps) / 4, q = c % 4;
+            uint32_t *dst = dig + j * dstride + dig_off(U, upl);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = b + th + 256 * u;
-            if (i < nq) {
-                const int j = i / per_slot, r = i % per_slot, U = r / XPLANES, p = r % XPLANES;
-                *(uint4 *)(dig + j * dstride + dig_off(U, upl) + 4 * p) = v[u];
+            for (int p = 0; p < XPLANES; ++p) dst[4 * p + q] = word[p];
+            if (q == 0) {
+                hsum[j * units + U] = sx;
+                hscl[j * units + U] = ldexpf(1.f, -E);
             }
         }
     }
-    for (int i = th; i < it.ntok * units; i += 256) {
-        hsum[i] = a.hsum[(size_t)it.slot0 * units + i];
-        hscl[i] = a.hscl[(size_t)it.slot0 * units + i];
-    }
+    (void)lane;
     __syncthreads();
-#define DQ(n) down_multi_tiles<BITS, n, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl)
-    NT_SWITCH(DQ)
-#undef DQ
+    if (it.ntok == 1) down_multi_tiles<BITS, 1, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
+    else down_multi_tiles<BITS, 2, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
 }
-
 
 // ------------------------------------------------------------- launchers
 inline bool gemv_supported_impl(int d, int f, int bits) {
@@ -798,25 +745,9 @@ inline bool gemv_supported_impl(int d, int f, int bits) {
     return true;
 }
 
-static inline int ntmax_for(int T) { return T >= CHUNK_TOK ? CHUNK_TOK : T; }
-// token capacity of a kernel instance: 1, 2, 4, 5 or 8
-static inline int nt_round(int nt) { return nt <= 2 ? nt : (nt <= 4 ? 4 : (nt <= 5 ? 5 : 8)); }
-
 // Every kernel here stays within the 64 KiB of LDS a block gets by default;
 // a launch that would need more is refused rather than attempted.
 constexpr size_t LDS_LIMIT = 64 * 1024;
-
-#define LAUNCH_NT(KER, BITS, nt, grid, block, lds, s, ...)                                           \
-    do {                                                                                             \
-        if ((lds) > LDS_LIMIT) return hipErrorInvalidValue;                                          \
-        switch (nt) {                                                                                \
-            case 1: STRATA_LAUNCH((KER<BITS, 1>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 2: STRATA_LAUNCH((KER<BITS, 2>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 4: STRATA_LAUNCH((KER<BITS, 4>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            case 5: STRATA_LAUNCH((KER<BITS, 5>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-            default: STRATA_LAUNCH((KER<BITS, 8>), grid, dim3(block), lds, s, __VA_ARGS__); break; \
-        }                                                                                            \
-    } while (0)
 
 // One token: 2-wave blocks of R columns of h per work item, plus the
 // routing writer.
@@ -825,65 +756,38 @@ template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_i
     const int off = gateup_lds_words(a.d, R, 1, 1);
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
     if (a.T != 1 || lds > LDS_LIMIT) return hipErrorInvalidValue;
-    STRATA_LAUNCH((gemv_gateup_small_kernel<BITS, 1>), dim3(max_items * (a.f / R) + 1), dim3(128), lds, s, a, R, off);
+    STRATA_LAUNCH(gemv_gateup_small_kernel<BITS>, dim3(max_items * (a.f / R) + 1), dim3(128), lds, s, a, R, off);
     return hipGetLastError();
 }
 
-// T <= 8 job loop: 32/R gate + 32/R up waves per block, about 8 waves per
-// compute unit (the job body holds two code tiles and up to ~250 VGPRs),
-// plus the routing writer.
+// T <= 8: 8-wave job-loop blocks, one per compute unit (a wave holds two
+// code tiles, ~200 VGPRs), plus the routing writer.
 template <int BITS> hipError_t gateup_multi_launch(const LayerArgs &a, int max_items, int cus, hipStream_t s) {
-    const int R = 64 / unit_slices(a.d, 8), G = 32 / R;
-    const int nt = nt_round(ntmax_for(a.T));
-    const int off = gateup_lds_words(a.d, R, a.T, nt) + nt * 32;
-    const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E) + 3 + small_route_table_words(a.T, a.k, a.E));
-    const int jobs = max_items * (a.f / 32);
-    const int grid = std::min(jobs, std::max(1, cus) * 4 / G) + 1;
-    const int upl = (a.d / 32) / (64 / R);
-    if (32 % R || lds > LDS_LIMIT) return hipErrorInvalidValue;
-    if (upl % 4 == 0) {
-        switch (nt) {
-            case 1: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 1, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 2: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 2, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 4: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 4, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 5: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 5, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            default: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 8, true>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-        }
-    } else {
-        switch (nt) {
-            case 1: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 1, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 2: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 2, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 4: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 4, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            case 5: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 5, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-            default: STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, 8, false>), dim3(grid), dim3(128 * G), lds, s, a, R, off); break;
-        }
-    }
+    const int R = 64 / unit_slices(a.d, 8), upl = (a.d / 32) / (64 / R);
+    const int off = gateup_lds_words(a.d, R, a.T, ITEM_TOK);
+    const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E) + 3 + small_route_table_words(a.T, a.k));
+    const int jobs = max_items * (a.f / (R / 2)), wpb = 8;
+    const int grid = std::min((jobs + wpb - 1) / wpb, std::max(1, cus)) + 1;
+    if (R % 2 || a.f % (R / 2) || lds > LDS_LIMIT || a.T > CHUNK_TOK) return hipErrorInvalidValue;
+    if (upl % 4 == 0)
+        STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, true>), dim3(grid), dim3(64 * wpb), lds, s, a, R, off);
+    else
+        STRATA_LAUNCH((gemv_gateup_multi_kernel<BITS, false>), dim3(grid), dim3(64 * wpb), lds, s, a, R, off);
     return hipGetLastError();
 }
 
 template <int BITS> hipError_t down_multi_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int R = 64 / unit_slices(a.f, 8), Q = 128 / (DN_WAVES * R);
-    const int nt = nt_round(ntmax_for(a.T));
-    const size_t lds = 4 * (size_t)down_multi_lds_words(a.f, R, nt);
+    const size_t lds = 4 * (size_t)down_multi_lds_words(a.f, R);
     const int upl = (a.f / 32) / (64 / R);
     if (Q < 1 || Q > DN_QMAX || a.d % 128 || lds > LDS_LIMIT) return hipErrorInvalidValue;
     const dim3 grid(max_items * (a.d / 128)), block(64 * DN_WAVES);
-#define DN_LAUNCH(UPLM)                                                                                                \
-    switch (nt) {                                                                                                      \
-        case 1: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 1, UPLM>), grid, block, lds, s, a, R, Q); break;          \
-        case 2: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 2, UPLM>), grid, block, lds, s, a, R, Q); break;          \
-        case 4: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 4, UPLM>), grid, block, lds, s, a, R, Q); break;          \
-        case 5: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 5, UPLM>), grid, block, lds, s, a, R, Q); break;          \
-        default: STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 8, UPLM>), grid, block, lds, s, a, R, Q); break;         \
-    }
-    if (upl == 3) {   // d_ff = 768: 3 units per lane
-        DN_LAUNCH(3)
-    } else if (upl == 1) {
-        DN_LAUNCH(1)
-    } else {
-        DN_LAUNCH(UPL_MAX)
-    }
-#undef DN_LAUNCH
+    if (upl == 3)   // d_ff = 768: 3 units per lane
+        STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 3>), grid, block, lds, s, a, R, Q);
+    else if (upl == 1)
+        STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 1>), grid, block, lds, s, a, R, Q);
+    else
+        STRATA_LAUNCH((gemv_down_multi_kernel<BITS, UPL_MAX>), grid, block, lds, s, a, R, Q);
     return hipGetLastError();
 }
 

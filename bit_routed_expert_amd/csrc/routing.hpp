@@ -244,12 +244,11 @@ __device__ __forceinline__ bool small_route_item(const LayerArgs &a, const Small
     return true;
 }
 
-// Every work item of this routing, in small_route_item's order, into LDS
-// (whole block): itab[4i .. 4i+3] = expert, first slot, token count, packed
-// token map.  Returns the number of items.  small_route_table_words(T, k, E)
-// words of itab.
-__host__ __device__ constexpr int small_route_table_words(int T, int k, int E) {
-    return 4 * ((T * k < E ? T * k : E) + 1);
+// Every work item of this routing, in the order small_route_write lists
+// them, into LDS (whole block): itab[4i .. 4i+3] = expert, first slot,
+// token count, packed token map.  Returns the number of items.
+__host__ __device__ constexpr int small_route_table_words(int T, int k) {
+    return 4 * (T * k + (T + ITEM_TOK - 1) / ITEM_TOK);
 }
 __device__ __forceinline__ int small_route_table(const LayerArgs &a, const SmallRoute &L, int32_t *itab) {
     const int th = threadIdx.x, nth = blockDim.x;
@@ -259,8 +258,9 @@ __device__ __forceinline__ int small_route_table(const LayerArgs &a, const Small
     for (int j = 0; j < ept; ++j) {
         const int e = th * ept + j;
         if (e < E) {
-            c_loc += __popc((uint32_t)L.tokmask[e]);
-            a_loc += (L.picked[e >> 5] >> (e & 31)) & 1u;
+            const int c = __popc((uint32_t)L.tokmask[e]);
+            c_loc += c;
+            a_loc += is_resident(a.mask, e) ? (c + ITEM_TOK - 1) / ITEM_TOK : 0;
         }
     }
     int tot;
@@ -270,21 +270,29 @@ __device__ __forceinline__ int small_route_table(const LayerArgs &a, const Small
         const int e = th * ept + j;
         if (e < E) {
             const uint32_t mk = (uint32_t)L.tokmask[e];
-            if ((L.picked[e >> 5] >> (e & 31)) & 1u) {
-                uint32_t rest = mk, tpk = 0;
-                for (int q = 0; rest; ++q) {
-                    tpk |= (uint32_t)(__ffs(rest) - 1) << (3 * q);
-                    rest &= rest - 1u;
+            const int c = __popc(mk);
+            if (is_resident(a.mask, e)) {
+                uint32_t rest = mk;
+                for (int q = 0; q < c; q += ITEM_TOK) {
+                    uint32_t tpk = 0;
+                    for (int i = 0; i < ITEM_TOK && rest; ++i) {
+                        tpk |= (uint32_t)(__ffs(rest) - 1) << (3 * i);
+                        rest &= rest - 1u;
+                    }
+                    *(int4 *)(itab + 4 * ai) = make_int4(e, off + q, min(ITEM_TOK, c - q), (int)tpk);
+                    ++ai;
                 }
-                *(int4 *)(itab + 4 * ai) = make_int4(e, off, __popc(mk), (int)tpk);
-                ++ai;
             }
-            off += __popc(mk);
+            off += c;
         }
     }
-    if (th == 0) *(int4 *)(itab + 4 * (tot >> 16)) = make_int4(E, n, T, (int)TOK_IDENTITY);
+    if (th == 0) {
+        for (int q = 0; q < T; q += ITEM_TOK)
+            *(int4 *)(itab + 4 * ((tot >> 16) + q / ITEM_TOK)) =
+                make_int4(E, n + q, min(ITEM_TOK, T - q), (int)(TOK_IDENTITY >> (3 * q)));
+    }
     __syncthreads();
-    return (tot >> 16) + 1;
+    return (tot >> 16) + (T + ITEM_TOK - 1) / ITEM_TOK;
 }
 
 // One block: write the routing outputs (ids, gates, counts, offsets,
@@ -305,7 +313,7 @@ __device__ __forceinline__ void small_route_write(const LayerArgs &a, const Smal
         if (e < E) {
             const int c = __popc((uint32_t)L.tokmask[e]);
             c_loc += c;
-            a_loc += (c > 0 && is_resident(a.mask, e)) ? 1 : 0;
+            a_loc += is_resident(a.mask, e) ? (c + ITEM_TOK - 1) / ITEM_TOK : 0;
         }
     }
     int tot;
@@ -319,15 +327,16 @@ __device__ __forceinline__ void small_route_write(const LayerArgs &a, const Smal
             a.offsets[e] = off;
             if (a.u_counts) a.u_counts[e] = c;
             if (a.u_offsets) a.u_offsets[e] = off;
-            if (c > 0 && is_resident(a.mask, e)) a.items[ai++] = WorkItem{e, off, (int32_t)c};
+            if (is_resident(a.mask, e))
+                for (int q = 0; q < c; q += ITEM_TOK) a.items[ai++] = WorkItem{e, off + q, min(ITEM_TOK, c - q)};
             off += c;
         }
     }
     if (th == 0) {
         a.offsets[E] = tot & 0xFFFF;
         if (a.u_offsets) a.u_offsets[E] = tot & 0xFFFF;
-        a.items[tot >> 16] = WorkItem{E, n, T};
-        *a.n_items = (tot >> 16) + 1;
+        for (int q = 0; q < T; q += ITEM_TOK) a.items[(tot >> 16) + q / ITEM_TOK] = WorkItem{E, n + q, min(ITEM_TOK, T - q)};
+        *a.n_items = (tot >> 16) + (T + ITEM_TOK - 1) / ITEM_TOK;
     }
     // slot of pick (t, r): offset of its expert + earlier tokens of that expert
     if (th < n) {
