@@ -411,8 +411,8 @@ __global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int
 // once (from the router logits, while every token's input digit planes load
 // into LDS) and list the work items (an expert's slots in pairs) in LDS;
 // then every wave runs its own jobs, job = (work item, R/2 columns of h),
-// jobs wave_id, wave_id + total waves, ..., the next job's codes loading
-// into a second named tile while the current one computes.  In a job, lane
+// jobs wave_id, wave_id + total waves, ..., the codes of the next two jobs
+// loading into two more named tiles while the current one computes.  In a job, lane
 // rows r < R/2 are gate rows and r >= R/2 the same rows of up, so h =
 // silu(g) * u forms inside the wave (no block barrier) and goes to hf; the
 // down kernel quantises it.  The last block writes the routing outputs and
@@ -473,7 +473,9 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     const int half = R / 2, groups = a.f / half;
     const int njobs = small_route_table(a, L, itab) * groups;   // last block barrier
     const int wpb = blockDim.x >> 6, nw = (gridDim.x - 1) * wpb;
-    int job = blockIdx.x * wpb + (threadIdx.x >> 6);
+    // job (and the item words read for it) are wave-uniform: say so, so the
+    // job loop is scalar control flow
+    int job = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (threadIdx.x >> 6));
     if (job >= njobs) return;
     const int lane = threadIdx.x & 63, rl = lane % R, m = rl >= half ? 1 : 0, U0 = (lane / R) * upl;
     const size_t mat_bytes = (size_t)a.d * a.f * BITS / 8, mat_blocks = (size_t)a.d * a.f / 256;
@@ -486,31 +488,39 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     uint32_t tpk;
     {
         const int4 v = *(const int4 *)(itab + 4 * (job / groups));
-        it = WorkItem{v.x, v.y, v.z};
-        tpk = (uint32_t)v.w;
+        it = WorkItem{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                      __builtin_amdgcn_readfirstlane(v.z)};
+        tpk = (uint32_t)__builtin_amdgcn_readfirstlane(v.w);
     }
-    // two tiles used alternately (named, no copies)
-    UTile<BITS> b0, b1;
+    // three tiles used in rotation (named, no copies): one computes while
+    // the codes of the next two jobs load
+    UTile<BITS> b0, b1, b2;
     GU_LOAD(b0, it, job);
-#define GU_STEP(CUR, NXT)                                                                                              \
+    {
+        const int nj = job + nw < njobs ? job + nw : job;
+        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));
+        GU_LOAD(b1, (WorkItem{__builtin_amdgcn_readfirstlane(v1.x), 0, 0}), nj);
+    }
+#define GU_STEP(CUR, NXT2)                                                                                             \
     {                                                                                                                  \
-        const int next = job + nw;                                                                                     \
-        const bool has = next < njobs;                                                                                 \
-        const int nj = has ? next : job; /* past the end: re-read this job's tile (cached) */                          \
-        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));                                                     \
-        const WorkItem it1{v1.x, v1.y, v1.z};                                                                          \
-        GU_LOAD(NXT, it1, nj);                                                                                         \
+        const int next = job + nw, next2 = job + 2 * nw;                                                               \
+        const int nj2 = next2 < njobs ? next2 : job; /* past the end: re-read this job's tile (cached) */              \
+        const int4 v2 = *(const int4 *)(itab + 4 * (nj2 / groups));                                                    \
+        GU_LOAD(NXT2, (WorkItem{__builtin_amdgcn_readfirstlane(v2.x), 0, 0}), nj2);                                    \
         const int c0 = (job % groups) * half;                                                                          \
         if (it.ntok == 1) gateup_wave_job<BITS, 1>(a, it, tpk, R, c0, g, CUR);                                         \
         else gateup_wave_job<BITS, 2>(a, it, tpk, R, c0, g, CUR);                                                      \
-        if (!has) break;                                                                                               \
+        if (next >= njobs) break;                                                                                      \
         job = next;                                                                                                    \
-        it = it1;                                                                                                      \
-        tpk = (uint32_t)v1.w;                                                                                          \
+        const int4 v1 = *(const int4 *)(itab + 4 * (job / groups));                                                    \
+        it = WorkItem{__builtin_amdgcn_readfirstlane(v1.x), __builtin_amdgcn_readfirstlane(v1.y),                      \
+                      __builtin_amdgcn_readfirstlane(v1.z)};                                                           \
+        tpk = (uint32_t)__builtin_amdgcn_readfirstlane(v1.w);                                                          \
     }
     for (;;) {
-        GU_STEP(b0, b1)
+        GU_STEP(b0, b2)
         GU_STEP(b1, b0)
+        GU_STEP(b2, b1)
     }
 #undef GU_STEP
 #undef GU_LOAD
@@ -692,24 +702,41 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
     if (item >= *a.n_items) return;
     const WorkItem it = a.items[item];
     const int row0 = (blockIdx.x % chunks) * rows_blk + wave * Q * R;
+    // loads in the order they are used: this thread's h chunk, then the code
+    // tiles (all unconditional, so each wait covers only what it needs)
+    const int cps = f / 8, nch = it.ntok * cps;   // 8-column chunks of the item's h rows
+    constexpr int HPER = (ITEM_TOK * MAX_HUNITS * 4 + 255) / 256;   // chunks per thread
+    float4 hv[2 * HPER];
+#pragma unroll
+    for (int u = 0; u < HPER; ++u) {
+        const int cc = min(th + 256 * u, nch - 1);
+        const float4 *src = (const float4 *)(a.hf + (size_t)it.slot0 * f) + 2 * cc;
+        hv[2 * u] = src[0];
+        hv[2 * u + 1] = src[1];
+    }
     const size_t mi = (size_t)it.expert * 3 + 2;
+    const uint8_t *mcodes = a.codes + mi * ((size_t)d * f * BITS / 8);
+    const uint16_t *mscl = a.scales + mi * ((size_t)d * f / 256);
     UTile<BITS, UPLM> wt[DN_QMAX];
 #pragma unroll
-    for (int q = 0; q < DN_QMAX; ++q)
-        if (q < Q)
-            wt[q].load(a.codes + mi * ((size_t)d * f * BITS / 8), a.scales + mi * ((size_t)d * f / 256), f,
-                       row0 + q * R, R, upl);
+    for (int q = 0; q < DN_QMAX; ++q) {
+        const int r = row0 + (q < Q ? q : 0) * R + lane % R;
+        if constexpr (UPLM % 4 == 0)
+            utile_load_all<BITS, true, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl);
+        else
+            utile_load_all<BITS, false, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl);
+    }
     const int dstride = units * XPLANES * 4 + S * 4;
     uint32_t *dig = lds;
     int *hsum = (int *)(lds + ITEM_TOK * dstride);
     float *hscl = (float *)(hsum + ITEM_TOK * units);
-    // quantise the item's h rows: chunk c (8 columns) of slot j = c / (f/8)
-    const int cps = f / 8, nch = it.ntok * cps;
-    for (int b = 0; b < nch; b += 256) {   // uniform trip count: every lane takes part in the shuffles
-        const int c = b + th, cc = min(c, nch - 1);
-        const float4 *src = (const float4 *)(a.hf + (size_t)it.slot0 * f) + 2 * cc;
-        const float4 v0 = src[0], v1 = src[1];
-        const float h[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    // quantise the item's h rows: chunk c (8 columns) of slot j = c / (f/8);
+    // the 4 chunks of a unit sit in 4 neighbouring lanes
+#pragma unroll
+    for (int u = 0; u < HPER; ++u) {
+        const int c = th + 256 * u;
+        const float h[8] = {hv[2 * u].x, hv[2 * u].y, hv[2 * u].z, hv[2 * u].w,
+                            hv[2 * u + 1].x, hv[2 * u + 1].y, hv[2 * u + 1].z, hv[2 * u + 1].w};
         float mx = 0.f;
 #pragma unroll
         for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
@@ -721,17 +748,16 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
         sx += __shfl_xor(sx, 1, WAVE);
         sx += __shfl_xor(sx, 2, WAVE);
         if (c < nch) {
-            const int j = c / cps, U = (c % cps) / 4, q = c % 4;
+            const int j = c / cps, U = (c % cps) / 4, qq = c % 4;
             uint32_t *dst = dig + j * dstride + dig_off(U, upl);
 #pragma unroll
-            for (int p = 0; p < XPLANES; ++p) dst[4 * p + q] = word[p];
-            if (q == 0) {
+            for (int p = 0; p < XPLANES; ++p) dst[4 * p + qq] = word[p];
+            if (qq == 0) {
                 hsum[j * units + U] = sx;
                 hscl[j * units + U] = ldexpf(1.f, -E);
             }
         }
     }
-    (void)lane;
     __syncthreads();
     if (it.ntok == 1) down_multi_tiles<BITS, 1, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
     else down_multi_tiles<BITS, 2, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
