@@ -411,8 +411,8 @@ __global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int
 // once (from the router logits, while every token's input digit planes load
 // into LDS) and list the work items (an expert's slots in pairs) in LDS;
 // then every wave runs its own jobs, job = (work item, R/2 columns of h),
-// jobs wave_id, wave_id + total waves, ..., the codes of the next two jobs
-// loading into two more named tiles while the current one computes.  In a job, lane
+// jobs wave_id, wave_id + total waves, ..., the next job's codes loading
+// into a second named tile while the current one computes.  In a job, lane
 // rows r < R/2 are gate rows and r >= R/2 the same rows of up, so h =
 // silu(g) * u forms inside the wave (no block barrier) and goes to hf; the
 // down kernel quantises it.  The last block writes the routing outputs and
@@ -492,35 +492,28 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
                       __builtin_amdgcn_readfirstlane(v.z)};
         tpk = (uint32_t)__builtin_amdgcn_readfirstlane(v.w);
     }
-    // three tiles used in rotation (named, no copies): one computes while
-    // the codes of the next two jobs load
-    UTile<BITS> b0, b1, b2;
+    // two tiles used alternately (named, no copies): one computes while the
+    // next job's codes load into the other
+    UTile<BITS> b0, b1;
     GU_LOAD(b0, it, job);
-    {
-        const int nj = job + nw < njobs ? job + nw : job;
-        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));
-        GU_LOAD(b1, (WorkItem{__builtin_amdgcn_readfirstlane(v1.x), 0, 0}), nj);
-    }
-#define GU_STEP(CUR, NXT2)                                                                                             \
+#define GU_STEP(CUR, NXT)                                                                                              \
     {                                                                                                                  \
-        const int next = job + nw, next2 = job + 2 * nw;                                                               \
-        const int nj2 = next2 < njobs ? next2 : job; /* past the end: re-read this job's tile (cached) */              \
-        const int4 v2 = *(const int4 *)(itab + 4 * (nj2 / groups));                                                    \
-        GU_LOAD(NXT2, (WorkItem{__builtin_amdgcn_readfirstlane(v2.x), 0, 0}), nj2);                                    \
+        const int next = job + nw;                                                                                     \
+        const int nj = next < njobs ? next : job; /* past the end: re-read this job's tile (cached) */                 \
+        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));                                                     \
+        GU_LOAD(NXT, (WorkItem{__builtin_amdgcn_readfirstlane(v1.x), 0, 0}), nj);                                      \
         const int c0 = (job % groups) * half;                                                                          \
         if (it.ntok == 1) gateup_wave_job<BITS, 1>(a, it, tpk, R, c0, g, CUR);                                         \
         else gateup_wave_job<BITS, 2>(a, it, tpk, R, c0, g, CUR);                                                      \
         if (next >= njobs) break;                                                                                      \
         job = next;                                                                                                    \
-        const int4 v1 = *(const int4 *)(itab + 4 * (job / groups));                                                    \
         it = WorkItem{__builtin_amdgcn_readfirstlane(v1.x), __builtin_amdgcn_readfirstlane(v1.y),                      \
                       __builtin_amdgcn_readfirstlane(v1.z)};                                                           \
         tpk = (uint32_t)__builtin_amdgcn_readfirstlane(v1.w);                                                          \
     }
     for (;;) {
-        GU_STEP(b0, b2)
+        GU_STEP(b0, b1)
         GU_STEP(b1, b0)
-        GU_STEP(b2, b1)
     }
 #undef GU_STEP
 #undef GU_LOAD
