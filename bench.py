@@ -51,7 +51,7 @@ CSRC = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
 WORKLOADS = {
     "decode": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=16, inputs=None,
                    sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
-    "mtp_verify": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=48, inputs=4,
+    "mtp_verify": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_multi_kernel", rotate=48, inputs=4,
                        sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
     "prefill_2bit": dict(kernel="gemm_gateup", symbol="gemm_gateup_kernel", rotate=2, inputs=4,
                          sources=["common.hpp", "mfma.hpp", "gemm_impl.hpp", "gemm_gu2.hip"]),
@@ -364,7 +364,7 @@ def traffic_summary(args):
         for c, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
             fh.write(f"cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv "
                      f"-d $REPO/gpurun_out/pmc_{tag} -o run -- python3 $REPO/bench.py --workload {args.workload} "
-                     f"--steps 50 --warmup 10 --profile-only --copy-calibration {args.copy_calibration}\n")
+                     f"--steps 20 --warmup 4 --profile-only --copy-calibration {args.copy_calibration}\n")
         fh.write(f"python3 bench.py --workload {args.workload} --copy-calibration {args.copy_calibration} "
                  "--traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
                  "gpurun_out/pmc_write/run_counter_collection.csv\n```\n\n")
