@@ -350,7 +350,8 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
         for (int v = 0; v < 16; ++v) {
             const int m = mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             const float g = acc.A0[mi][v], u = acc.A1[mi][v];
-            const float hv = g / (1.f + expf(-g)) * u;
+            // silu(g) * u with the hardware 2^x and reciprocal (about 1 ulp each)
+            const float hv = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
             const uint16_t hi = f2bf(hv);
             const float hif = bf16_to_float(hi);
             const uint16_t lo = f2bf(hv - hif);
@@ -362,11 +363,8 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
             }
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) ssum[v] += __shfl_xor(ssum[v], o, WAVE);
-        }
-        if (n == 0) {
+        for (int v = 0; v < 16; ++v) ssum[v] = half_wave_sum(ssum[v]);
+        if (n == 31) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
