@@ -375,7 +375,7 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
 }
 
 template <int BITS, int PASSES>
-__global__ __launch_bounds__(256, 2) void gemm_gateup_kernel(LayerArgs a, int nft) {
+__global__ __launch_bounds__(256, PASSES == 1 ? 3 : 2) void gemm_gateup_kernel(LayerArgs a, int nft) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[PASSES * GEMM_BM * GROW];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[PASSES * GEMM_BM * GROW];
     __shared__ float lds_s[GMAX_STEPS * GEMM_BM];   // [step][row]
@@ -447,7 +447,7 @@ template <int BITS>
 __global__ __launch_bounds__(256, 2) void gemm_down_kernel(LayerArgs a, int nft) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[2 * GEMM_BM * GROW];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[2 * GEMM_BM * GROW];
-    __shared__ float lds_s[GMAX_STEPS * GEMM_BM];
+    extern __shared__ float lds_s[];   // [scale block of the f features][row]
     int tile, ft;
     if (!pick_tile(nft, *a.n_items, tile, ft)) return;
     const WorkItem it = a.items[tile];
@@ -468,7 +468,8 @@ template <int BITS, int PASSES> hipError_t gemm_gateup_launch(const LayerArgs &a
 template <int BITS> hipError_t gemm_down_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int nft = (a.d + 255) / 256;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
-    STRATA_LAUNCH((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
+    const size_t lds_s = sizeof(float) * GEMM_BM * (a.f / ((a.f & 255) ? 128 : 256));   // S per scale block and row
+    STRATA_LAUNCH((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), lds_s, s, a, nft);
     return hipGetLastError();
 }
 
