@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
 }
 
 // Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e] on the bf16
-// matrix cores.  Wr (fp32) is split into three bf16 pieces, exactly; x is
+// matrix cores.  Wr (fp32) is split into three bf16 pieces, exactly, once per
+// call (route_split_kernel); x is
 // one piece when it is bf16, else three (products of pieces below 2^-32 of
 // the leading one are dropped).  Every product is exact in fp32; each
 // 256-column block is summed on its own and the block sums are added with
@@ -184,6 +185,26 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
 // rounding.  Block tile 128 tokens x 64 experts; wave w owns tokens
 // 32*w .. +32 against all 64 experts (two 32x32 MFMA tiles).
 constexpr int RT_T = 128, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
+
+// Wr as three exact bf16 pieces, once per call: wp[q][e][i], Wr = hi + mid + lo.
+__global__ __launch_bounds__(256) void route_split_kernel(LayerArgs a) {
+    const int64_t n8 = (int64_t)a.E * a.d / 8, c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= n8) return;
+    const float4 *src = (const float4 *)(a.Wr + 8 * c);
+    const float4 w0 = src[0], w1 = src[1];
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint16_t hw[3][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split3(w[j], hw[0][j], hw[1][j], hw[2][j]);
+    const int64_t plane = (int64_t)a.E * a.d;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        uint32_t u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = (uint32_t)hw[q][2 * j] | ((uint32_t)hw[q][2 * j + 1] << 16);
+        *(uint4 *)(a.wp + q * plane + 8 * c) = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+}
 
 template <int PX>
 __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
@@ -197,9 +218,10 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
     const int xr = th >> 1, xc = (th & 1) * 16;
     const int wr = th >> 2, wc = (th & 3) * 8;
     const int64_t xoff = (int64_t)min(t0 + xr, T - 1) * d + xc;
-    const float *wrow = a.Wr + (int64_t)min(e0 + wr, E - 1) * d + wc;
+    const int64_t woff = (int64_t)min(e0 + wr, E - 1) * d + wc, plane = (int64_t)E * d;
     const bool wvalid = e0 + wr < E;
-    float xv[16], wv8[8];
+    float xv[16];
+    uint4 wq[3];   // 8 columns of this thread's Wr row as three bf16 pieces
     auto load = [&](int k0) __attribute__((always_inline)) {
         if (a.x_is_bf16) {
             const uint4 *p = (const uint4 *)((const uint16_t *)a.x + xoff + k0);
@@ -218,9 +240,8 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
                 xv[4 * j] = q.x; xv[4 * j + 1] = q.y; xv[4 * j + 2] = q.z; xv[4 * j + 3] = q.w;
             }
         }
-        const float4 w0 = *(const float4 *)(wrow + k0), w1 = *(const float4 *)(wrow + k0 + 4);
-        wv8[0] = w0.x; wv8[1] = w0.y; wv8[2] = w0.z; wv8[3] = w0.w;
-        wv8[4] = w1.x; wv8[5] = w1.y; wv8[6] = w1.z; wv8[7] = w1.w;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) wq[q] = *(const uint4 *)(a.wp + q * plane + woff + k0);
     };
     f32x16_t P[2], acc[2], comp[2];
 #pragma unroll
@@ -246,16 +267,9 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
                 dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
                 dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
             }
-            uint16_t hw[3][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) split3(wvalid ? wv8[j] : 0.f, hw[0][j], hw[1][j], hw[2][j]);
-#pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                uint32_t w[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] = (uint32_t)hw[q][2 * j] | ((uint32_t)hw[q][2 * j + 1] << 16);
-                *(uint4 *)(ws[q] + wr * RT_RS + wc) = make_uint4(w[0], w[1], w[2], w[3]);
-            }
+            for (int q = 0; q < 3; ++q)
+                *(uint4 *)(ws[q] + wr * RT_RS + wc) = wvalid ? wq[q] : make_uint4(0u, 0u, 0u, 0u);
         }
         __syncthreads();
         if (k0 + RT_K < d) load(k0 + RT_K);
@@ -461,6 +475,8 @@ hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
     const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T);
     if (a.d % RT_K) return hipErrorInvalidValue;
+    const int64_t n8 = (int64_t)a.E * a.d / 8;
+    STRATA_LAUNCH(route_split_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a);
     if (a.x_is_bf16)
         STRATA_LAUNCH(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
     else
