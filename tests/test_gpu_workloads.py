@@ -191,3 +191,28 @@ def test_route_only_entry_point():
         t.cuda.synchronize()
         G.assert_route_equal({kk: v.cpu().numpy() for kk, v in out.items()},
                              dict(idx=idx, gate=gate, counts=counts, offsets=offsets, perm=perm, pos=pos))
+
+
+@pytest.mark.parametrize("bits,T", [(3, 1), (3, 8), (2, 5)])
+def test_wide_topk_and_shared_picks(bits, T):
+    """E = 32, k = 12: k + 1 work items exceed the one-token down kernel's
+    waves, so a single token also takes the multi-token kernels; a router
+    bias makes every token pick the same 12 experts, so each expert's slots
+    split into several two-slot work items.  Outputs match the oracle, and
+    the batch equals one-token calls bit for bit."""
+    w = synth.Workload(f"wide_b{bits}", 32, 12, 256, 128, bits, T, seed=0x5EED00A1 + bits)
+    L = W.layer_data(w, 0)
+    bias = np.zeros(w.n_experts, np.float32)
+    bias[[1, 4, 5, 7, 10, 13, 17, 19, 22, 25, 28, 31]] = 50.0
+    L["bias"] = bias
+    x, _ = W.draw_tokens(w, L["Wr"], bias, range(T), rep=17)
+    print(f"case wide top-k bits={bits} T={T}", flush=True)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, synth.bf16_to_f32(x), L["Wr"],
+                           L["codes"], L["scales"], bias=bias)
+    dl = [G.layer_to_dev(L)]
+    got = G.run_forward(w, dl, G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    for t in range(T if T > 1 else 0):
+        one = G.run_forward(w, dl, G.dev(x[t:t + 1]), 0, 1, want_route=False)
+        np.testing.assert_array_equal(one["y"][0], got["y"][t])
