@@ -35,6 +35,20 @@ template <typename T> __device__ __forceinline__ T wave_sum(T v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
     return v;
 }
+// Sum over the wave by DPP (no LDS round trips): row sums by quad permutes
+// and row rotations, then row 0 into row 1, row 2 into row 3, and lane 31
+// into rows 2 and 3; the total is complete in lanes 48..63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define WS_DPP(CTRL, ROWS) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false))
+    v += WS_DPP(0xB1, 0xF);    // quad_perm [1,0,3,2]
+    v += WS_DPP(0x4E, 0xF);    // quad_perm [2,3,0,1]
+    v += WS_DPP(0x124, 0xF);   // row_ror:4
+    v += WS_DPP(0x128, 0xF);   // row_ror:8
+    v += WS_DPP(0x142, 0xA);   // row_bcast:15 into rows 1 and 3
+    v += WS_DPP(0x143, 0xC);   // row_bcast:31 into rows 2 and 3
+#undef WS_DPP
+    return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));

@@ -691,9 +691,9 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
     const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
     const int d = a.d, f = a.f, units = f / 32, S = 64 / R, upl = units / S;
     const int rows_blk = DN_WAVES * Q * R, chunks = d / rows_blk;
-    const int item = blockIdx.x / chunks;
+    const int item = blockIdx.x / chunks;   // < max_items: the list slot exists
+    const WorkItem it = a.items[item];      // read together with the count (one round trip)
     if (item >= *a.n_items) return;
-    const WorkItem it = a.items[item];
     const int row0 = (blockIdx.x % chunks) * rows_blk + wave * Q * R;
     // loads in the order they are used: this thread's h chunk, then the code
     // tiles (all unconditional, so each wait covers only what it needs)

@@ -156,11 +156,11 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
                         acc += wv[j].x * xv.x + wv[j].y * xv.y + wv[j].z * xv.z + wv[j].w * xv.w;
                     }
                 }
-                zacc[t] += wave_sum(acc);
+                zacc[t] += wave_sum_dpp(acc);   // complete in lanes 48..63
             }
         }
     }
-    if (lane == 0 && e < E) {
+    if (lane == 63 && e < E) {
 #pragma unroll
         for (int t = 0; t < CHUNK_TOK; ++t)
             if (t < T) a.z[t * E + e] = zacc[t];
