@@ -591,7 +591,7 @@ __host__ __device__ inline int down_one_lds_words(int k, int f, int R) {
     return (k + 1) * R + (k + 1) * (units * XPLANES * 4 + S * 4 + 2 * units) + 3 * k;
 }
 
-template <int BITS>
+template <int BITS, int UPLM>
 __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, int R) {
     extern __shared__ uint32_t lds[];
     const int th = threadIdx.x, wave = th >> 6, lane = th & 63, NW = blockDim.x >> 6;
@@ -617,19 +617,22 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
         pg = a.gate[lane];
         pp = a.pos[lane];
     }
+    // the work item is read together with the count (items holds k + 1 entries, so slot `wave` exists)
+    const WorkItem it = a.items[wave < k ? wave : k];
     const int n = *a.n_items;
     if (wave < n) {
-        const WorkItem it = a.items[wave];
         if (!fast) {
             slot = it.slot0;
             st.load(a, slot);
         }
-        UTile<BITS> wt;
-        wt.load(a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
-                a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f, row0, R, upl);
+        UTile<BITS, UPLM> wt;   // loads issued unconditionally: the waits that follow cover only what they need
+        utile_load_all<BITS, UPLM % 4 == 0, UPLM>(wt, a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
+                                                  a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f,
+                                                  row0 + lane % R, (lane / R) * upl, upl);
         st.store(a, upl, dstride, wdig, wsum, wscl);
         float res[1];
-        utile_compute<BITS, 1>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS, TOK_IDENTITY, res);
+        utile_compute<BITS, 1, UPLM>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS,
+                                     TOK_IDENTITY, res);
         if (lane < R) ybuf[slot * R + lane] = res[0];
     }
     if (wave == 0 && lane < k) {
@@ -815,7 +818,14 @@ template <int BITS> hipError_t down_one_launch(const LayerArgs &a, hipStream_t s
     const int R = 64 / unit_slices(a.f, 8);
     const size_t lds = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
     if (a.T != 1 || lds > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
-    STRATA_LAUNCH(gemv_down_rows_one_kernel<BITS>, dim3(a.d / R), dim3(64 * (a.k + 1)), lds, s, a, R);
+    const int upl = (a.f / 32) / (64 / R);
+    const dim3 grid(a.d / R), block(64 * (a.k + 1));
+    if (upl == 3)   // d_ff = 768
+        STRATA_LAUNCH((gemv_down_rows_one_kernel<BITS, 3>), grid, block, lds, s, a, R);
+    else if (upl == 1)
+        STRATA_LAUNCH((gemv_down_rows_one_kernel<BITS, 1>), grid, block, lds, s, a, R);
+    else
+        STRATA_LAUNCH((gemv_down_rows_one_kernel<BITS, UPL_MAX>), grid, block, lds, s, a, R);
     return hipGetLastError();
 }
 
