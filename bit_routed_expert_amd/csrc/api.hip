@@ -56,7 +56,7 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
     l.counter = take(ALIGN);
-    l.z = take(sizeof(float) * T * E);
+    l.z = take(sizeof(float) * T * E * (sp ? 1 : route_logit_splits((int)d)));
     l.idx = take(4 * T * k);
     l.gate = take(4 * T * k);
     l.counts = take(4 * E);
@@ -107,6 +107,7 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.bits = s.bits;
     a.T = T;
     a.z = (float *)(ws + l.z);
+    a.zsplit = small_path(s, T) ? 1 : route_logit_splits(s.d_model);
     a.idx = (int32_t *)(ws + l.idx);
     a.gate = (float *)(ws + l.gate);
     a.counts = (int32_t *)(ws + l.counts);

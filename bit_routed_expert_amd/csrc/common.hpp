@@ -138,7 +138,8 @@ struct LayerArgs {
     int x_is_bf16;
     int normalize;
     // routing state (internal)
-    float *z;            // [T][E] logits
+    float *z;            // [T][E] logits; larger T: [zsplit][T][E] partial sums over column ranges
+    int zsplit;          // column ranges of the larger-T router (1 on the decode path)
     int32_t *idx;        // [T][k]
     float *gate;         // [T][k]
     int32_t *counts;     // [E]
@@ -203,6 +204,7 @@ hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemv_gateup_multi(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);
+int route_logit_splits(int d);
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_permute(const LayerArgs &a, int tile, hipStream_t s);
 int route_perm_blocks(int T);

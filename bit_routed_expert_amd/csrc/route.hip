@@ -175,14 +175,16 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
     small_route_write(a, L);
 }
 
-// Router logits z[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias[e] on the bf16
-// matrix cores.  Wr (fp32) is split into three bf16 pieces, exactly, once per
-// call (route_split_kernel); x is
-// one piece when it is bf16, else three (products of pieces below 2^-32 of
-// the leading one are dropped).  Every product is exact in fp32; each
-// 256-column block is summed on its own and the block sums are added with
-// compensated (Kahan) summation, so the logit error stays near one fp32
-// rounding.  Block tile 128 tokens x 64 experts; wave w owns tokens
+// Router dot products x[t] . Wr[e] on the bf16 matrix cores (the logit is
+// inv_rms[t] times this plus bias[e], formed by the top-k kernel).  Wr (fp32)
+// is split into three bf16 pieces, exactly, once per call
+// (route_split_kernel); x is one piece when it is bf16, else three (products
+// of pieces below 2^-32 of the leading one are dropped).  Every product is
+// exact in fp32; each 256-column block is summed on its own and the block
+// sums are added in order.  The columns are cut into zsplit equal ranges of
+// whole blocks (grid z), each written as its own partial plane of z, so the
+// grid has enough blocks to hide memory latency; the top-k kernel adds the
+// planes in order.  Block tile 128 tokens x 64 experts; wave w owns tokens
 // 32*w .. +32 against all 64 experts (two 32x32 MFMA tiles).
 constexpr int RT_T = 128, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
 
@@ -207,13 +209,14 @@ __global__ __launch_bounds__(256) void route_split_kernel(LayerArgs a) {
 }
 
 template <int PX>
-__global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256, 4) void route_logits_mfma_kernel(LayerArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[PX][RT_T * RT_RS];
     __shared__ __attribute__((aligned(16))) uint16_t ws[3][RT_E * RT_RS];
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int t0 = blockIdx.y * RT_T, e0 = blockIdx.x * RT_E;
     const int d = a.d, T = a.T, E = a.E;
+    const int kspan = d / a.zsplit, kbeg = blockIdx.z * kspan, kend = kbeg + kspan;
     // staging: x rows th/2 (16 columns each), Wr rows th/4 (8 columns each)
     const int xr = th >> 1, xc = (th & 1) * 16;
     const int wr = th >> 2, wc = (th & 3) * 8;
@@ -243,13 +246,13 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
 #pragma unroll
         for (int q = 0; q < 3; ++q) wq[q] = *(const uint4 *)(a.wp + q * plane + woff + k0);
     };
-    f32x16_t P[2], acc[2], comp[2];
+    f32x16_t P[2], acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) P[j][v] = acc[j][v] = comp[j][v] = 0.f;
-    load(0);
-    for (int k0 = 0; k0 < d; k0 += RT_K) {
+        for (int v = 0; v < 16; ++v) P[j][v] = acc[j][v] = 0.f;
+    load(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += RT_K) {
         __syncthreads();
         {   // pieces into LDS
             uint16_t hx[PX][16];
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
                 *(uint4 *)(ws[q] + wr * RT_RS + wc) = wvalid ? wq[q] : make_uint4(0u, 0u, 0u, 0u);
         }
         __syncthreads();
-        if (k0 + RT_K < d) load(k0 + RT_K);
+        if (k0 + RT_K < kend) load(k0 + RT_K);
 #pragma unroll
         for (int kk = 0; kk < RT_K; kk += 16) {
             bf16x8_t A[PX], B[2][3];
@@ -296,37 +299,57 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(LayerArgs a) {
                 }
             }
         }
-        if (((k0 + RT_K) & 255) == 0 || k0 + RT_K >= d) {
+        if (((k0 + RT_K) & 255) == 0 || k0 + RT_K >= kend) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float y = P[j][v] - comp[j][v];
-                    const float t = acc[j][v] + y;
-                    comp[j][v] = (t - acc[j][v]) - y;
-                    acc[j][v] = t;
+                    acc[j][v] += P[j][v];
                     P[j][v] = 0.f;
                 }
         }
     }
+    float *zp = a.z + (int64_t)blockIdx.z * T * E;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = e0 + j * 32 + n;
         if (e >= E) continue;
-        const float b = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int t = t0 + wv * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (t < T) a.z[(int64_t)t * E + e] = acc[j][v] * a.inv_rms[t] + b;
+            if (t < T) zp[(int64_t)t * E + e] = acc[j][v];
         }
     }
 }
 
-// One wave per token.
+// One wave per token: the partial planes of z added in order into LDS, then
+// the logits inv_rms[t] * z + bias and their top-k.
 __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ float zrow[4][1024];
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= a.T) return;
-    wave_topk(a.z + (size_t)t * a.E, a.E, a.k, 1.f, nullptr, a.idx + (size_t)t * a.k, a.gate + (size_t)t * a.k,
+    const int E = a.E, ns = a.zsplit;
+    float *zr = zrow[threadIdx.x >> 6];
+    // every load of the token's planes issued before the first add (E <= 1024, at most 4 planes)
+    float v[4][16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = lane + 64 * j;
+            v[q][j] = (q < ns && e < E) ? a.z[((size_t)q * a.T + t) * E + e] : 0.f;
+        }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = lane + 64 * j;
+        float acc = v[0][j];
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (q < ns) acc += v[q][j];
+        if (e < E) zr[e] = acc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the row is read back by other lanes
+    wave_topk(zr, E, a.k, a.inv_rms[t], a.bias, a.idx + (size_t)t * a.k, a.gate + (size_t)t * a.k,
               a.u_idx ? a.u_idx + (size_t)t * a.k : nullptr, a.u_gate ? a.u_gate + (size_t)t * a.k : nullptr,
               nullptr, nullptr);
 }
@@ -472,9 +495,16 @@ hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Column ranges of the larger-T router: up to 4, each a whole number of 256-column blocks.
+int route_logit_splits(int d) {
+    int ks = 4;
+    while (ks > 1 && d % (ks * 256)) ks >>= 1;
+    return ks;
+}
+
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
-    const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T);
-    if (a.d % RT_K) return hipErrorInvalidValue;
+    const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T, a.zsplit);
+    if (a.d % RT_K || a.zsplit < 1 || a.d % a.zsplit || (a.d / a.zsplit) % RT_K || a.E > 1024) return hipErrorInvalidValue;
     const int64_t n8 = (int64_t)a.E * a.d / 8;
     STRATA_LAUNCH(route_split_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a);
     if (a.x_is_bf16)
@@ -485,6 +515,7 @@ hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route_topk(const LayerArgs &a, hipStream_t s) {
+    if (a.E > 1024 || a.zsplit < 1 || a.zsplit > 4) return hipErrorInvalidValue;
     STRATA_LAUNCH(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
