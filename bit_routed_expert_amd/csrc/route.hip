@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
 // each block's first miss-list entry, and the work list; route_scatter:
 // the stable rank of every pick inside its block (per-expert token
 // bitmaps), perm/pos and the miss list in (t, r) order.
-constexpr int PERM_T = 256;
+constexpr int PERM_T = 64;
 
 __global__ __launch_bounds__(256) void route_count_kernel(LayerArgs a) {
     __shared__ int hist[1024];
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(256) void route_count_kernel(LayerArgs a) {
     }
     __syncthreads();
     for (int e = th; e < E; e += 256) a.bcnt[(int64_t)b * E + e] = hist[e];
-    int tot;
-    block_excl_scan(nmiss, tmp, &tot);
+    int tot = 0;
+    if (a.mask) block_excl_scan(nmiss, tmp, &tot);
     if (th == 0) a.bmiss[b] = tot;
 }
 
@@ -388,8 +388,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(LayerArgs a, int nb, i
     const int th = threadIdx.x, E = a.E, T = a.T;
     const int64_t n = (int64_t)T * a.k;
     int c = 0;
-    if (th < E)
+    if (th < E) {
+#pragma unroll 8
         for (int b = 0; b < nb; ++b) c += a.bcnt[(int64_t)b * E + th];
+    }
     int tot;
     const int off = block_excl_scan(c, tmp, &tot);
     if (th < E) {
@@ -398,6 +400,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(LayerArgs a, int nb, i
         if (a.u_counts) a.u_counts[th] = c;
         if (a.u_offsets) a.u_offsets[th] = off;
         int run = off;
+#pragma unroll 8
         for (int b = 0; b < nb; ++b) {   // in place: count -> first slot of the block
             const int v = a.bcnt[(int64_t)b * E + th];
             a.bcnt[(int64_t)b * E + th] = run;
@@ -459,6 +462,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(LayerArgs a) {
         if (a.u_pos) a.u_pos[g0 + i] = slot;
     }
     // miss list entries of this block, in pick order (t asc, r asc)
+    if (!a.mask) return;
     int mrun = a.bmiss[b];
     for (int i0 = 0; i0 < nt * k; i0 += 256) {
         const int i = i0 + th;
