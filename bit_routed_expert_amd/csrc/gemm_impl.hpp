@@ -89,6 +89,29 @@ template <> __device__ __forceinline__ Raw<2> load_unit<2>(const uint8_t *p) {
     return Raw<2>{v.x, v.y};
 }
 
+// Buffer resources: a block-uniform base and size (scalar registers), so a
+// load is the lane's 32-bit offset plus a uniform offset in a scalar
+// register, with no per-lane address arithmetic; reads past the size return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+template <int BITS> __device__ __forceinline__ Raw<BITS> load_unit_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                                     uint32_t soff);
+template <> __device__ __forceinline__ Raw<3> load_unit_buf<3>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    return Raw<3>{v[0], v[1], v[2]};
+}
+template <> __device__ __forceinline__ Raw<2> load_unit_buf<2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return Raw<2>{v[0], v[1]};
+}
+// A pointer known to be the same in every lane, in scalar registers.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const void *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+}
+
 template <int G> __device__ __forceinline__ bf16x8_t decode_group3(const Raw<3> &r, uint32_t M, uint32_t B) {
     uint32_t W;
     if (G == 0) W = r.w0;
@@ -144,15 +167,18 @@ __device__ __forceinline__ bool pick_tile(int nft, int n_items, int &tile, int &
 
 // Stage LDS step s (64 K positions) of the block's A rows into dst: each
 // wave moves three groups of 8 rows per pass, 16 bytes per lane, straight
-// into LDS (rows of pass p at dst + p * GEMM_BM * GROW).
+// into LDS (rows of pass p at dst + p * GEMM_BM * GROW).  Addresses are a
+// block-uniform base (scalar registers) plus this lane's 32-bit byte offset.
 template <int PASSES>
-__device__ __forceinline__ void stage_a(const uint16_t *const arow[3], int64_t pass_stride, int s,
+__device__ __forceinline__ void stage_a(__amdgpu_buffer_rsrc_t ar, const uint32_t aoff[3], uint32_t pass_bytes, int s,
                                         uint8_t *__restrict__ dst, int wv) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
 #pragma unroll
         for (int q = 0; q < 3; ++q)
-            lds_dma16(arow[q] + p * pass_stride + s * GSUB, dst + p * GEMM_BM * GROW + (wv * 3 + q) * 8 * GROW);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ar, (__attribute__((address_space(3))) void *)(dst + p * GEMM_BM * GROW + (wv * 3 + q) * 8 * GROW), 16,
+                aoff[q], p * pass_bytes + (uint32_t)s * GSUB * 2, 0, 0);
 }
 
 // byte offset of the code unit a lane reads at LDS step s (relative to unit 2h of step 0)
@@ -236,12 +262,13 @@ __device__ __forceinline__ void enter_block(Acc2<BITS, NMT> &acc, const float *_
 
 // Main K loop shared by both GEMMs: stage s+1 (A by DMA, codes into
 // registers) while step s runs on the matrix cores; enter a new scale
-// block every CH columns.  p0/p1: code unit of this lane for the two slices
+// block every CH columns.  cr0 + co0 / cr1 + co1: code unit of this lane for the two slices
 // at step 0; sc0p/sc1p + (row*in + c) / 256: their scales.
 template <int BITS, int PASSES, int NMT>
 __device__ __forceinline__ void k_loop(Acc2<BITS, NMT> &acc, uint8_t *__restrict__ buf0, uint8_t *__restrict__ buf1,
-                                       const float *__restrict__ lds_s, const uint16_t *const arow[3],
-                                       int64_t pass_stride, const uint8_t *p0, const uint8_t *p1,
+                                       const float *__restrict__ lds_s, __amdgpu_buffer_rsrc_t ar,
+                                       const uint32_t aoff[3], uint32_t pass_bytes, __amdgpu_buffer_rsrc_t cr0,
+                                       uint32_t co0, __amdgpu_buffer_rsrc_t cr1, uint32_t co1,
                                        const uint16_t *sc0p, const uint16_t *sc1p, int64_t rin0, int64_t rin1,
                                        int in, bool active, int wv, int n, int h) {
     const int nsub = in / GSUB;
@@ -252,18 +279,18 @@ __device__ __forceinline__ void k_loop(Acc2<BITS, NMT> &acc, uint8_t *__restrict
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc.A0[mi][v] = acc.A1[mi][v] = 0.f;
     acc.s0 = acc.s1 = 1.f;
-    Raw<BITS> ra0 = load_unit<BITS>(p0), rb0 = load_unit<BITS>(p1);
+    Raw<BITS> ra0 = load_unit_buf<BITS>(cr0, co0, 0), rb0 = load_unit_buf<BITS>(cr1, co1, 0);
     Raw<BITS> ra1 = ra0, rb1 = rb0;
     uint16_t q0 = sc0p[rin0 >> 8], q1 = sc1p[rin1 >> 8];
-    stage_a<PASSES>(arow, pass_stride, 0, buf0, wv);
+    stage_a<PASSES>(ar, aoff, pass_bytes, 0, buf0, wv);
     wait_vmem();
     __syncthreads();
     for (int s = 0; s < nsub; s += 2) {
         // even step: compute from buf0, stage into buf1
-        stage_a<PASSES>(arow, pass_stride, s + 1, buf1, wv);
+        stage_a<PASSES>(ar, aoff, pass_bytes, s + 1, buf1, wv);
         if (active) {
-            ra1 = load_unit<BITS>(p0 + b_off<BITS>(s + 1));
-            rb1 = load_unit<BITS>(p1 + b_off<BITS>(s + 1));
+            ra1 = load_unit_buf<BITS>(cr0, co0, (uint32_t)b_off<BITS>(s + 1));
+            rb1 = load_unit_buf<BITS>(cr1, co1, (uint32_t)b_off<BITS>(s + 1));
             if (s % spc == 0) {
                 enter_block<BITS, NMT>(acc, lds_s, s / spc, q0, q1, n, h);
                 if (s + spc < nsub) {   // next block's scales
@@ -278,11 +305,11 @@ __device__ __forceinline__ void k_loop(Acc2<BITS, NMT> &acc, uint8_t *__restrict
         __syncthreads();
         // odd step: compute from buf1, stage into buf0
         const bool more = s + 2 < nsub;
-        if (more) stage_a<PASSES>(arow, pass_stride, s + 2, buf0, wv);
+        if (more) stage_a<PASSES>(ar, aoff, pass_bytes, s + 2, buf0, wv);
         if (active) {
             if (more) {
-                ra0 = load_unit<BITS>(p0 + b_off<BITS>(s + 2));
-                rb0 = load_unit<BITS>(p1 + b_off<BITS>(s + 2));
+                ra0 = load_unit_buf<BITS>(cr0, co0, (uint32_t)b_off<BITS>(s + 2));
+                rb0 = load_unit_buf<BITS>(cr1, co1, (uint32_t)b_off<BITS>(s + 2));
             }
             mfma_step<BITS, PASSES, NMT>(buf1, ra1, rb1, acc, n, h);
         }
@@ -323,20 +350,22 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
         const float *p = a.sx + (int64_t)lds_tok[m] * nsteps + cb * spb;
         lds_s[i] = spb == 2 ? p[0] + p[1] : p[0];
     }
-    const uint16_t *arow[3];
+    uint32_t aoff[3];   // byte offsets into xa (< 2^31: checked by the launcher)
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         const int m = (wv * 3 + q) * 8 + (lane >> 3);
-        arow[q] = a.xa + (int64_t)lds_tok[m] * d + 8 * ((lane & 7) ^ a_swz(m));
+        aoff[q] = 2u * ((uint32_t)lds_tok[m] * (uint32_t)d + 8u * ((lane & 7) ^ a_swz(m)));
     }
     const int j0 = ft * 128 + wv * 32, r = j0 + n;
-    const uint8_t *cg = a.codes + (int64_t)it.expert * ((int64_t)3 * d * f * BITS / 8);
-    const uint8_t *cu = cg + (int64_t)f * d * BITS / 8;
+    const uint32_t mbytes = (uint32_t)((int64_t)f * d * BITS / 8);   // one packed matrix
+    const uint8_t *cg = uniform_ptr(a.codes + (int64_t)it.expert * 3 * mbytes);
+    const uint8_t *cu = cg + mbytes;
     const uint16_t *sg = a.scales + (int64_t)it.expert * ((int64_t)3 * d * f / 256);
     const uint16_t *su = sg + (int64_t)f * d / 256;
     Acc2<BITS, NMT> acc;
-    k_loop<BITS, PASSES, NMT>(acc, buf0, buf1, lds_s, arow, (int64_t)T * d, cg + unit_off<BITS>(r, 2 * h, d),
-                              cu + unit_off<BITS>(r, 2 * h, d), sg, su, (int64_t)r * d, (int64_t)r * d, d, true,
+    const uint32_t co = (uint32_t)unit_off<BITS>(r, 2 * h, d);
+    k_loop<BITS, PASSES, NMT>(acc, buf0, buf1, lds_s, buf_rsrc(a.xa, (uint32_t)PASSES * T * d * 2), aoff,
+                              (uint32_t)T * d * 2, buf_rsrc(cg, mbytes), co, buf_rsrc(cu, mbytes), co, sg, su, (int64_t)r * d, (int64_t)r * d, d, true,
                               wv, n, h);
     // h = silu(g) * u as a bf16 hi/lo pair at its permuted position, and
     // per-row sums of hi + lo over this wave's 32 features
@@ -413,20 +442,23 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it
         for (int q = 0; q < gpb; ++q) acc += p[q];
         lds_s[i] = acc;
     }
-    const uint16_t *arow[3];
+    uint32_t aoff[3];   // byte offsets into ha (< 2^31: checked by the launcher)
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         const int m = (wv * 3 + q) * 8 + (lane >> 3);
-        arow[q] = a.ha + (it.slot0 + min(m, ntok - 1)) * f + 8 * ((lane & 7) ^ a_swz(m));
+        aoff[q] = 2u * ((uint32_t)(it.slot0 + min(m, ntok - 1)) * (uint32_t)f + 8u * ((lane & 7) ^ a_swz(m)));
     }
     const int j0 = ft * 256 + wv * 64;
     const bool active = j0 < d;
     const int r0 = min(j0, d - 64) + n, r1 = r0 + 32;
-    const uint8_t *cd = a.codes + (int64_t)it.expert * ((int64_t)3 * d * f * BITS / 8) + (int64_t)2 * f * d * BITS / 8;
+    const uint32_t mbytes = (uint32_t)((int64_t)f * d * BITS / 8);   // one packed matrix
+    const uint8_t *cd = uniform_ptr(a.codes + ((int64_t)it.expert * 3 + 2) * mbytes);
     const uint16_t *sd = a.scales + (int64_t)it.expert * ((int64_t)3 * d * f / 256) + (int64_t)2 * f * d / 256;
     Acc2<BITS, NMT> acc;
-    k_loop<BITS, 2, NMT>(acc, buf0, buf1, lds_s, arow, slots * f, cd + unit_off<BITS>(r0, 2 * h, f),
-                         cd + unit_off<BITS>(r1, 2 * h, f), sd, sd, (int64_t)r0 * f, (int64_t)r1 * f, f, active,
+    const __amdgpu_buffer_rsrc_t cr = buf_rsrc(cd, mbytes);
+    k_loop<BITS, 2, NMT>(acc, buf0, buf1, lds_s, buf_rsrc(a.ha, (uint32_t)(2 * slots * f * 2)), aoff,
+                         (uint32_t)(slots * f * 2), cr, (uint32_t)unit_off<BITS>(r0, 2 * h, f), cr,
+                         (uint32_t)unit_off<BITS>(r1, 2 * h, f), sd, sd, (int64_t)r0 * f, (int64_t)r1 * f, f, active,
                          wv, n, h);
     if (!active) return;
 #pragma unroll
@@ -444,7 +476,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256, 2) void gemm_down_kernel(LayerArgs a, int nft) {
+__global__ __launch_bounds__(256, 3) void gemm_down_kernel(LayerArgs a, int nft) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[2 * GEMM_BM * GROW];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[2 * GEMM_BM * GROW];
     extern __shared__ float lds_s[];   // [scale block of the f features][row]
@@ -461,6 +493,7 @@ __global__ __launch_bounds__(256, 2) void gemm_down_kernel(LayerArgs a, int nft)
 template <int BITS, int PASSES> hipError_t gemm_gateup_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int nft = a.f / 128;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
+    if ((int64_t)PASSES * a.T * a.d * 2 > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // 32-bit buffer offsets into xa
     STRATA_LAUNCH((gemm_gateup_kernel<BITS, PASSES>), dim3((unsigned)blocks), dim3(256), 0, s, a, nft);
     return hipGetLastError();
 }
@@ -469,6 +502,7 @@ template <int BITS> hipError_t gemm_down_launch(const LayerArgs &a, int max_item
     const int nft = (a.d + 255) / 256;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
     const size_t lds_s = sizeof(float) * GEMM_BM * (a.f / ((a.f & 255) ? 128 : 256));   // S per scale block and row
+    if (((int64_t)a.T * a.k + a.T) * a.f * 4 > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // buffer offsets into ha
     STRATA_LAUNCH((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), lds_s, s, a, nft);
     return hipGetLastError();
 }
