@@ -371,13 +371,19 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
     // per-row sums of hi + lo over this wave's 32 features
     const int64_t slots = Tk + T;
     const int pos = (r & ~127) + step_pos(r & 127);
-    uint16_t *hhi = a.ha, *hlo = a.ha + slots * f;
+    // stores go through buffer resources spanning the tile's ntok rows, so
+    // rows past ntok fall outside them and are dropped by the hardware
+    const uint32_t rowb = 2u * f, nf = f / 32;
+    const __amdgpu_buffer_rsrc_t rhi = buf_rsrc(uniform_ptr(a.ha + it.slot0 * f), ntok * rowb);
+    const __amdgpu_buffer_rsrc_t rlo = buf_rsrc(uniform_ptr(a.ha + (slots + it.slot0) * f), ntok * rowb);
+    const __amdgpu_buffer_rsrc_t rhs = buf_rsrc(uniform_ptr(a.hs + it.slot0 * nf), ntok * nf * 4);
+    const uint32_t vo = 4u * h * rowb + 2u * pos, vs = 4u * (4u * h * nf + (j0 >> 5));
 #pragma unroll
     for (int mi = 0; mi < NMT; ++mi) {
         float ssum[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int m = mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const uint32_t ml = mi * 32 + 8 * (v >> 2) + (v & 3);   // tile row minus 4h
             const float g = acc.A0[mi][v], u = acc.A1[mi][v];
             // silu(g) * u with the hardware 2^x and reciprocal (about 1 ulp each)
             const float hv = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
@@ -385,19 +391,16 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
             const float hif = bf16_to_float(hi);
             const uint16_t lo = f2bf(hv - hif);
             ssum[v] = hif + bf16_to_float(lo);
-            if (m < ntok) {
-                const int64_t slot = it.slot0 + m;
-                hhi[slot * f + pos] = hi;
-                hlo[slot * f + pos] = lo;
-            }
+            __builtin_amdgcn_raw_buffer_store_b16(hi, rhi, vo + ml * rowb, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(lo, rlo, vo + ml * rowb, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) ssum[v] = half_wave_sum(ssum[v]);
         if (n == 31) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int m = mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < ntok) a.hs[(it.slot0 + m) * (f / 32) + (j0 >> 5)] = ssum[v];
+                const uint32_t ml = mi * 32 + 8 * (v >> 2) + (v & 3);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ssum[v]), rhs, vs + ml * nf * 4, 0, 0);
             }
         }
     }
@@ -461,16 +464,17 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it
                          (uint32_t)unit_off<BITS>(r1, 2 * h, f), sd, sd, (int64_t)r0 * f, (int64_t)r1 * f, f, active,
                          wv, n, h);
     if (!active) return;
+    // rows past ntok fall outside the resource and are dropped
+    const uint32_t rowb = 4u * d;
+    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(uniform_ptr(a.Y + it.slot0 * d), ntok * rowb);
+    const uint32_t vo = 4u * h * rowb + 4u * r0;
 #pragma unroll
     for (int mi = 0; mi < NMT; ++mi) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int m = mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (m < ntok) {
-                float *y = a.Y + (it.slot0 + m) * d;
-                y[r0] = acc.A0[mi][v];
-                y[r1] = acc.A1[mi][v];
-            }
+            const uint32_t ml = mi * 32 + 8 * (v >> 2) + (v & 3);   // tile row minus 4h
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.A0[mi][v]), ry, vo + ml * rowb, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.A1[mi][v]), ry, vo + ml * rowb + 128, 0, 0);
         }
     }
 }
