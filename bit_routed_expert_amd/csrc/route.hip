@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void route_split_kernel(LayerArgs a) {
 }
 
 template <int PX>
-__global__ __launch_bounds__(256, 4) void route_logits_mfma_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel(LayerArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[PX][RT_T * RT_RS];
     __shared__ __attribute__((aligned(16))) uint16_t ws[3][RT_E * RT_RS];
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
