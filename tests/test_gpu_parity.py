@@ -208,3 +208,45 @@ def test_three_layer_stack_on_matrix_core_path(bits):
         u_gpu = oracle.layer_input(inputs[l], l)
         _, gate_g = oracle.select(oracle.logits(u_gpu, Ls[l]["Wr"]), w.top_k)
         assert np.max(np.abs(got["route"][l]["topk_w"] - gate_g)) <= G.GATE_TOL, f"layer {l} gates"
+
+
+@pytest.mark.parametrize("T", [1, 5, 12])
+def test_exact_logit_ties_break_by_lower_index(T):
+    """Router rows duplicated in pairs (expert 2i+1 has expert 2i's row), so
+    every logit occurs exactly twice and each pair is an exact tie that the
+    lower index wins; with k = 9 the ninth pick splits a pair.  Tokens keep
+    margins >= 1e-3 between distinct logits.  Decode kernels (T = 1, 5) and
+    the matrix-core path (T = 12)."""
+    base = synth.WORKLOADS["decode"]
+    w = synth.Workload("decode_k9", base.n_experts, 9, base.d_model, base.d_ff, base.bits, T, seed=base.seed + 0x79)
+    L = W.layer_data(w, 0)
+    Wr = L["Wr"].copy()
+    Wr[1::2] = Wr[0::2]
+    L["Wr"] = Wr
+    # margins over the distinct logits: half the experts, top 6 of them (the 9 picks span 5 pairs)
+    wd = synth.Workload("decode_k9_distinct", base.n_experts // 2, 6, base.d_model, base.d_ff, base.bits, T,
+                        seed=base.seed + 0x7A)
+    x, _ = W.draw_tokens(wd, Wr[0::2], None, range(T), rep=29)
+    print(f"case paired router rows k=9 T={T}", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    assert np.all(ref["idx"][:, 8] % 2 == 0) and np.all(ref["idx"][:, 0::2] % 2 == 0)   # each pair's lower index first
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+
+
+@pytest.mark.parametrize("T", [1, 12])
+def test_zero_router_picks_lowest_indices(T):
+    """A zero router: all 512 logits tie, so every token picks experts 0..k-1
+    in index order with equal gates (more than 64 keys reach the threshold,
+    which exercises the round-by-round selection)."""
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 0)
+    L["Wr"] = np.zeros_like(L["Wr"])
+    x = synth.x_tokens(w, np.arange(T), np.zeros(T, np.int64), 31)
+    print(f"case zero router T={T}", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    np.testing.assert_array_equal(ref["idx"], np.tile(np.arange(w.top_k), (T, 1)))
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
