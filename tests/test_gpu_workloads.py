@@ -216,3 +216,23 @@ def test_wide_topk_and_shared_picks(bits, T):
     for t in range(T if T > 1 else 0):
         one = G.run_forward(w, dl, G.dev(x[t:t + 1]), 0, 1, want_route=False)
         np.testing.assert_array_equal(one["y"][0], got["y"][t])
+
+
+@pytest.mark.parametrize("E,k,d,f,bits,T", [(1024, 8, 256, 128, 3, 1), (1024, 8, 256, 128, 3, 5),
+                                            (1024, 8, 256, 128, 2, 20), (1000, 6, 384, 384, 3, 1),
+                                            (1000, 6, 384, 384, 2, 5), (1000, 6, 384, 384, 3, 20)])
+def test_wide_expert_counts_and_odd_widths(E, k, d, f, bits, T):
+    """More than 512 experts (16 logits per lane in the top-k, the largest
+    supported expert count), an expert count that is not a multiple of 64,
+    and d = f = 384 (rows of 1.5 scale blocks, 12 units per row: 128-column
+    scale steps on the matrix-core path) on the decode kernels (T = 1, 5)
+    and the matrix-core path (T = 20)."""
+    w = synth.Workload(f"wide_E{E}_d{d}_b{bits}", E, k, d, f, bits, T, seed=0x5EED0B00 + E + d + bits)
+    L = W.layer_data(w, 0)
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=13)
+    print(f"case E={E} k={k} d={d} f={f} bits={bits} T={T}", flush=True)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, synth.bf16_to_f32(x), L["Wr"],
+                           L["codes"], L["scales"])
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
