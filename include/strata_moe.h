@@ -50,7 +50,9 @@
  *   allocates on these entry points and keeps no per-call global state.
  *   Calls enqueue on `stream` (a hipStream_t, passed as void*) and return
  *   without a host synchronisation; outputs are valid once the stream is
- *   synchronised.  Validation happens on the host before any launch and
+ *   synchronised.  They enqueue kernel launches only (no memset, copy or
+ *   event unless events are passed), so a call can be captured in a HIP
+ *   graph and replayed with new contents in the same buffers.  Validation happens on the host before any launch and
  *   nothing is enqueued when it fails.  Calls that overlap on one workspace
  *   race.
  *   The workspace must be zero-filled before its first use; every call
