@@ -339,10 +339,18 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     const size_t mat_bytes = (size_t)d * f * BITS / 8;
     const size_t mat_blocks = (size_t)d * f / 256;
     const size_t mi = (size_t)it.expert * 3 + m;
+    // this wave's staging loads (issued before the routing) have landed; the
+    // code loads then go out unconditionally and stay in flight across the
+    // barrier, which waits only for LDS (each use waits for its own unit)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     UTile<BITS> wt;
-    wt.load(a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, row0, R, upl);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
-    __syncthreads();                                  // every wave's staged digit planes visible
+    const int r = row0 + lane % R, U0 = (lane / R) * upl;
+    if (upl % 4 == 0)
+        utile_load_all<BITS, true>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl);
+    else
+        utile_load_all<BITS, false>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
+    __builtin_amdgcn_s_barrier();         // every wave's staged digit planes and sums visible
     float res[NT];
     utile_compute<BITS, NT>(wt, R, upl, unit_period(d, XGROUP_UNITS), g.dig, g.dstride, g.sum, g.units, g.scl, g.G,
                             XGROUP_UNITS, tpk, res);
