@@ -762,7 +762,10 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
             }
         }
     }
-    __syncthreads();
+    // LDS-only barrier: the code tiles stay in flight, so the first tile's
+    // products start as soon as its own loads land
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
+    __builtin_amdgcn_s_barrier();
     if (it.ntok == 1) down_multi_tiles<BITS, 1, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
     else down_multi_tiles<BITS, 2, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
 }
