@@ -479,7 +479,12 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     __builtin_amdgcn_s_waitcnt(0);
     int32_t *itab = (int32_t *)(lds + ((route_off + small_route_lds_words(a.E) + 3) & ~3));   // 16-byte aligned
     const int half = R / 2, groups = a.f / half;
-    const int njobs = small_route_table(a, L, itab) * groups;   // last block barrier
+    const int nitems = small_route_table(a, L, itab);   // last block barrier
+    const int njobs = nitems * groups;
+    // jobs walk the table from its end: the shared expert's items (every
+    // token, two per item) go out in the first rounds and the last rounds
+    // hold one-token routed items, which shortens the tail
+#define GU_ITEM(JOB_) (nitems - 1 - (JOB_) / groups)
     const int wpb = blockDim.x >> 6, nw = (gridDim.x - 1) * wpb;
     // job (and the item words read for it) are wave-uniform: say so, so the
     // job loop is scalar control flow
@@ -495,7 +500,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     WorkItem it;
     uint32_t tpk;
     {
-        const int4 v = *(const int4 *)(itab + 4 * (job / groups));
+        const int4 v = *(const int4 *)(itab + 4 * GU_ITEM(job));
         it = WorkItem{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                       __builtin_amdgcn_readfirstlane(v.z)};
         tpk = (uint32_t)__builtin_amdgcn_readfirstlane(v.w);
@@ -508,7 +513,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     {                                                                                                                  \
         const int next = job + nw;                                                                                     \
         const int nj = next < njobs ? next : job; /* past the end: re-read this job's tile (cached) */                 \
-        const int4 v1 = *(const int4 *)(itab + 4 * (nj / groups));                                                     \
+        const int4 v1 = *(const int4 *)(itab + 4 * GU_ITEM(nj));                                                       \
         GU_LOAD(NXT, (WorkItem{__builtin_amdgcn_readfirstlane(v1.x), 0, 0}), nj);                                      \
         const int c0 = (job % groups) * half;                                                                          \
         if (it.ntok == 1) gateup_wave_job<BITS, 1>(a, it, tpk, R, c0, g, CUR);                                         \
@@ -525,6 +530,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     }
 #undef GU_STEP
 #undef GU_LOAD
+#undef GU_ITEM
 }
 
 // ----------------------------------------------------------------- down
