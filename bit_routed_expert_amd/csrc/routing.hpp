@@ -16,28 +16,50 @@ __device__ __forceinline__ uint32_t f32_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum / minimum of a 32-bit value over the wave (uniform result).
-template <bool MAX> __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
-#define RED_STEP(CTRL)                                                                         \
-    {                                                                                          \
-        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false); \
-        v = MAX ? (v > o ? v : o) : (v < o ? v : o);                                           \
+// Butterfly over the whole wave, every lane ending with the result and no
+// scalar hand-off: quad permutes and row mirrors combine each 16-lane row,
+// then the row swaps of gfx950 (16-lane rows, then 32-lane halves) pair each
+// lane with its partner row.  Every lane combines the same two operands, so
+// the result is the same bit pattern in all lanes.
+#define WAVE_BFLY(V, OP)                                                                                   \
+    {                                                                                                      \
+        V = OP(V, (decltype(V))__builtin_bit_cast(decltype(V), __builtin_amdgcn_update_dpp(              \
+                      0, __builtin_bit_cast(int, V), 0xB1, 0xF, 0xF, false))); /* quad_perm [1,0,3,2] */  \
+        V = OP(V, (decltype(V))__builtin_bit_cast(decltype(V), __builtin_amdgcn_update_dpp(              \
+                      0, __builtin_bit_cast(int, V), 0x4E, 0xF, 0xF, false))); /* quad_perm [2,3,0,1] */  \
+        V = OP(V, (decltype(V))__builtin_bit_cast(decltype(V), __builtin_amdgcn_update_dpp(              \
+                      0, __builtin_bit_cast(int, V), 0x141, 0xF, 0xF, false))); /* row_half_mirror */     \
+        V = OP(V, (decltype(V))__builtin_bit_cast(decltype(V), __builtin_amdgcn_update_dpp(              \
+                      0, __builtin_bit_cast(int, V), 0x140, 0xF, 0xF, false))); /* row_mirror */          \
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, V),                 \
+                                                          __builtin_bit_cast(uint32_t, V), false, false);  \
+        V = OP(__builtin_bit_cast(decltype(V), (uint32_t)p16[0]), __builtin_bit_cast(decltype(V), (uint32_t)p16[1])); \
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, V),                 \
+                                                          __builtin_bit_cast(uint32_t, V), false, false);  \
+        V = OP(__builtin_bit_cast(decltype(V), (uint32_t)p32[0]), __builtin_bit_cast(decltype(V), (uint32_t)p32[1])); \
     }
-    RED_STEP(0xB1) RED_STEP(0x4E) RED_STEP(0x141) RED_STEP(0x140)
-#undef RED_STEP
-    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
-    const uint32_t a = MAX ? (r0 > r1 ? r0 : r1) : (r0 < r1 ? r0 : r1);
-    const uint32_t b = MAX ? (r2 > r3 ? r2 : r3) : (r2 < r3 ? r2 : r3);
-    return MAX ? (a > b ? a : b) : (a < b ? a : b);
+__device__ __forceinline__ uint32_t bfly_umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t bfly_umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ float bfly_fadd(float a, float b) { return a + b; }
+__device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
+    WAVE_BFLY(v, bfly_umax)
+    return v;
 }
+__device__ __forceinline__ uint32_t wave_allmin_u32(uint32_t v) {
+    WAVE_BFLY(v, bfly_umin)
+    return v;
+}
+__device__ __forceinline__ float wave_allsum_f32(float v) {
+    WAVE_BFLY(v, bfly_fadd)
+    return v;
+}
+#undef WAVE_BFLY
 
 // Ordered top-k of E logits z[e] * scale + bias[e] by one wave (JM = E/64
 // rounded up to 8 or 16); lane r < k ends with pick r: *e_out, *z_out.  Each
 // lane sorts its JM candidates by (value desc, index asc); a round takes the
-// wave maximum of the lanes' head values (32-bit) and, only when several
-// lanes hold that value, the smallest of their head indices; the owning
-// lane pops its head.
+// wave maximum of the lanes' head values (32-bit), then the smallest head
+// index among the lanes holding it; the owning lane pops its head.
 template <int JM>
 __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
                                                      int *e_out, float *z_out) {
@@ -80,14 +102,10 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
     int my_e = 0;
     uint32_t my_k = 0x80000000u;   // key of 0.0 for lanes past k
     for (int r = 0; r < k; ++r) {
-        const uint32_t m = wave_reduce_u32<true>(kv[0]);
-        const uint64_t ball = __ballot(kv[0] == m);
-        uint32_t e;
-        if (__popcll(ball) == 1) {
-            e = (uint32_t)__builtin_amdgcn_readlane((int)ki[0], __ffsll((unsigned long long)ball) - 1);
-        } else {
-            e = wave_reduce_u32<false>(kv[0] == m ? ki[0] : 0xFFFFFFFFu);
-        }
+        // largest head value, then the smallest expert index among the
+        // lanes holding it; both land in every lane
+        const uint32_t m = wave_allmax_u32(kv[0]);
+        const uint32_t e = wave_allmin_u32(kv[0] == m ? ki[0] : 0xFFFFFFFFu);
         if (lane == r) {
             my_e = (int)e;
             my_k = m;
@@ -116,9 +134,9 @@ __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float sc
         wave_topk_picks_fast<8>(z, E, k, scale, bias, &e, &v);
     else
         wave_topk_picks_fast<16>(z, E, k, scale, bias, &e, &v);
-    const float top = __shfl(v, 0, WAVE);
+    const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float p = (lane < k) ? expf(v - top) : 0.f;
-    const float s = wave_sum(p);
+    const float s = wave_allsum_f32(p);
     if (lane < k) {
         const float g = p / s;
         if (idx_out) idx_out[lane] = e;
