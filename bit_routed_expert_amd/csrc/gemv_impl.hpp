@@ -368,11 +368,12 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     }
 }
 
-// One token: every block (2 waves, R columns of h) takes the
-// top-k itself from the router logits (a few KB) while its input digit
-// planes, unit sums and group scales load, derives its own work item and
-// runs it; the last block writes the routing outputs and the work list
-// instead.
+// One token: blocks of 2 waves, R columns of h each.  The first f/R
+// blocks take the shared expert and need no routing; every other group of
+// f/R blocks takes one pick: each block takes the top-k itself from the
+// router logits (a few KB, one wave) while the other wave stages the input
+// digit planes, unit sums and group scales, and runs its pick's rows; the
+// last block writes the routing outputs and the work list instead.
 template <int BITS>
 __global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
@@ -393,7 +394,16 @@ __global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int
         const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
         qv[u] = q < nq ? (i < g.units ? a.xsum[(size_t)j * g.units + i] : __float_as_int(a.xscl[(size_t)j * g.G + i - g.units])) : 0;
     }
-    small_route_compute(a, L, a.z, a.inv_rms);
+    const int cols = (blockDim.x >> 7) * R, wg_per_item = a.f / cols;
+    const int b = blockIdx.x / wg_per_item;   // 0: shared expert, else pick b - 1
+    if (b > 0 && threadIdx.x < 64) {
+        WorkItem r{};
+        const bool ok = one_token_item(a, b - 1, r);
+        if (threadIdx.x == 0) {
+            L.tmp[0] = ok ? r.expert : -1;
+            L.tmp[1] = r.slot0;
+        }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
@@ -407,12 +417,16 @@ __global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int
         if (i < g.units) g.sum[j * g.units + i] = a.xsum[(size_t)j * g.units + i];
         else g.scl[j * g.G + i - g.units] = a.xscl[(size_t)j * g.G + i - g.units];
     }
-    const int cols = (blockDim.x >> 7) * R, wg_per_item = a.f / cols;
-    WorkItem it;
-    uint32_t tpk;
-    if (!small_route_item(a, L, blockIdx.x / wg_per_item, it, tpk)) return;
+    WorkItem it{a.E, a.k, 1};
+    if (b > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the item is in LDS
+        __builtin_amdgcn_s_barrier();
+        const int ex = L.tmp[0];
+        if (ex < 0) return;   // a pick that is not resident (whole block)
+        it = WorkItem{ex, L.tmp[1], 1};
+    }
     const int j0 = (blockIdx.x % wg_per_item) * cols;
-    gateup_body<BITS, 1>(a, it, tpk, R, j0, g);
+    gateup_body<BITS, 1>(a, it, TOK_IDENTITY, R, j0, g);
 }
 
 // Any T <= 8 (the path for T >= 2).  Blocks take the top-k of all T tokens

@@ -219,46 +219,21 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
 constexpr uint32_t TOK_IDENTITY = 0xFAC688u;   // slot j -> token j
 __host__ __device__ __forceinline__ int tok_of(uint32_t tpk, int j) { return (int)((tpk >> (3 * j)) & 7u); }
 
-// Work item `item` of this routing, computed by every wave alike (no block
-// barrier): the item-th picked resident expert in ascending order, or, for
-// item == their number, the shared expert with all T tokens.  Slots of
-// expert e start at the number of picks of experts below e.  Returns false
-// past the last item.  tpk: packed token map (token of slot j = tok_of(tpk, j)).
-__device__ __forceinline__ bool small_route_item(const LayerArgs &a, const SmallRoute &L, int item, WorkItem &it,
-                                                 uint32_t &tpk) {
-    const int lane = threadIdx.x & 63, n = a.T * a.k;
-    const int c = lane < 32 ? __popc(L.picked[lane]) : 0;
-    int pre = c;   // inclusive prefix of the bitmap word counts
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-        const int t = __shfl_up(pre, o, WAVE);
-        if (lane >= o) pre += t;
-    }
-    const int nres = __shfl(pre, 31, WAVE);
-    if (item > nres) return false;
-    if (item == nres) {
-        it = WorkItem{a.E, n, a.T};
-        tpk = TOK_IDENTITY;
-        return true;
-    }
-    const int w = __ffsll((unsigned long long)__ballot(lane < 32 && pre > item)) - 1;
-    uint32_t word = L.picked[w];
-    for (int r = item - (__shfl(pre, w, WAVE) - __shfl(c, w, WAVE)); r > 0; --r) word &= word - 1u;
-    const int e = w * 32 + __ffs(word) - 1;
-    int below = 0;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        below += __popcll(__ballot(j < n && L.sidx[min(j, n - 1)] < e));
-    }
-    const uint32_t mk = (uint32_t)L.tokmask[e];
-    it = WorkItem{e, below, (int32_t)__popc(mk)};
-    uint32_t rest = mk;   // slot j: the j-th set bit of the token mask
-    tpk = 0;
-#pragma unroll
-    for (int j = 0; j < CHUNK_TOK; ++j) {
-        tpk |= (uint32_t)(rest ? __ffs(rest) - 1 : 0) << (3 * j);
-        rest &= rest - 1u;
-    }
+// One token, one wave: the picks alone (no gates, no LDS state) and the
+// work item of pick r (in top-k order): its expert and, as first slot, the
+// number of picks of lower experts (the slot small_route_write gives it).
+// Returns false when that expert is not resident.  Results are wave-uniform.
+__device__ __forceinline__ bool one_token_item(const LayerArgs &a, int r, WorkItem &it) {
+    const int lane = threadIdx.x & 63, k = a.k;
+    int e;
+    float v;
+    if (a.E <= 512)
+        wave_topk_picks_fast<8>(a.z, a.E, k, a.inv_rms[0], a.bias, &e, &v);
+    else
+        wave_topk_picks_fast<16>(a.z, a.E, k, a.inv_rms[0], a.bias, &e, &v);
+    const int er = __builtin_amdgcn_readlane(e, r);
+    if (!is_resident(a.mask, er)) return false;
+    it = WorkItem{er, (int)__popcll(__ballot(lane < k && e < er)), 1};
     return true;
 }
 
