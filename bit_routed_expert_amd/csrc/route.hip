@@ -214,9 +214,18 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
     __shared__ __attribute__((aligned(16))) uint16_t ws[3][RT_E * RT_RS];
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
     const int n = lane & 31, h = lane >> 5;
-    const int t0 = blockIdx.y * RT_T, e0 = blockIdx.x * RT_E;
+    // Blocks are dealt to the 8 XCDs round-robin by linear index; renumber
+    // them so that XCD c runs the c-th eighth of the (expert block fastest,
+    // then token block, then column range) order: the expert blocks sharing a
+    // token tile share that XCD's L2, and so do the token blocks of one column
+    // range of the router pieces.
+    const int nbx = gridDim.x, nby = gridDim.y, nb = nbx * nby * gridDim.z;
+    const int id = blockIdx.x + nbx * (blockIdx.y + nby * blockIdx.z);
+    const int li = (nb % 8 == 0) ? (id % 8) * (nb / 8) + id / 8 : id;
+    const int bx = li % nbx, by = (li / nbx) % nby, bz = li / (nbx * nby);
+    const int t0 = by * RT_T, e0 = bx * RT_E;
     const int d = a.d, T = a.T, E = a.E;
-    const int kspan = d / a.zsplit, kbeg = blockIdx.z * kspan, kend = kbeg + kspan;
+    const int kspan = d / a.zsplit, kbeg = bz * kspan, kend = kbeg + kspan;
     // staging: x rows th/2 (16 columns each), Wr rows th/4 (8 columns each)
     const int xr = th >> 1, xc = (th & 1) * 16;
     const int wr = th >> 2, wc = (th & 3) * 8;
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
                 }
         }
     }
-    float *zp = a.z + (int64_t)blockIdx.z * T * E;
+    float *zp = a.z + (int64_t)bz * T * E;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = e0 + j * 32 + n;
