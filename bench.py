@@ -55,6 +55,9 @@ WORKLOADS = {
                        sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
     "prefill_2bit": dict(kernel="gemm_gateup", symbol="gemm_gateup_kernel", rotate=2, inputs=4,
                          sources=["common.hpp", "mfma.hpp", "gemm_impl.hpp", "gemm_gu2.hip"]),
+    # one step = the whole 32K prompt: its eight 4096-token chunks, in order
+    "zipf_prefill": dict(kernel="gemm_gateup", symbol="gemm_gateup_kernel", rotate=2, inputs=8,
+                         sources=["common.hpp", "mfma.hpp", "gemm_impl.hpp", "gemm_gu3.hip"]),
 }
 COPY_SYMBOL = "MulFunctor"
 
@@ -63,22 +66,22 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
-                   help="timed steps (default 2000 decode, 200 prefill, 100 verify)")
+                   help="timed steps (default 2000 decode, 200 prefill, 100 verify, 30 Zipf prompts)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (default steps / 10)")
     p.add_argument("--rotate", type=int, default=None, help="independent resident layers cycled through")
     p.add_argument("--cpu-sample-s", type=float, default=12.0, help="target seconds of oracle work")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-only", action="store_true", help="skip the CPU baseline and event pass")
     p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS),
-                   help="decode (the headline line), the 48-layer T=5 verify step or the 4096-token 2-bit "
-                        "prefill chunk")
+                   help="decode (the headline line), the 48-layer T=5 verify step, the 4096-token 2-bit "
+                        "prefill chunk or the 32K-token Zipf-skewed prefill with the 165-expert resident mask")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run a plain fp32 elementwise copy of MIB MiB (read + write) 5 times before the warmup")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the traffic summary from two rocprofv3 counter CSVs of a --copy-calibration run")
     a = p.parse_args()
     if a.steps is None:
-        a.steps = {"decode": 2000, "mtp_verify": 100}.get(a.workload, 200)
+        a.steps = {"decode": 2000, "mtp_verify": 100, "zipf_prefill": 30}.get(a.workload, 200)
     if a.warmup is None:
         a.warmup = max(1, a.steps // 10)
     if a.rotate is None:
@@ -116,6 +119,10 @@ def main():
     dev = torch.device("cuda", 0)
 
     # ---- resident inputs: `rotate` independent layers + the token batches
+    calls = w.calls                     # forward calls per step (the prompt's chunks)
+    bias = torch.from_numpy(synth.zipf_bias(w)).to(dev) if w.zipf_s > 0 else None
+    mask_np = synth.resident_mask(w) if w.resident else None
+    mask = torch.from_numpy(mask_np.view(np.int32)).to(dev) if mask_np is not None else None
     nrot = args.rotate
     layer_bytes = w.experts_total * w.code_bytes_per_expert
     pinned = torch.empty(layer_bytes, dtype=torch.uint8, pin_memory=True)
@@ -127,10 +134,12 @@ def main():
         codes.copy_(pinned, non_blocking=False)
         scales = torch.from_numpy(synth.layer_scales(w, l).view(np.int16)).to(dev)
         wr = torch.from_numpy(synth.router_weights(w, l)).to(dev)
-        layers.append(brx.LayerData(router_w=wr, codes=codes, scales=scales))
+        layers.append(brx.LayerData(router_w=wr, codes=codes, scales=scales, router_bias=bias, resident_mask=mask))
     del pinned
     n_step = args.warmup + args.steps
     n_in = n_step if cfg["inputs"] is None else cfg["inputs"]   # a new token per decode step
+    if calls > 1 and n_in % calls:
+        sys.exit("the input batches must hold whole prompts")
     xs = torch.from_numpy(synth.x_tokens(w, range(n_in * T), rep=1).view(np.int16)).to(dev).view(n_in, T, d)
     setup_s = time.time() - t0
 
@@ -143,13 +152,20 @@ def main():
     resid = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     names = brx.kernel_names(sh, T)
+    miss = {}
+    if mask is not None:   # miss list of every (token, non-resident pick); T*k entries never overflow
+        cap = T * k
+        miss = dict(miss_te=torch.empty((cap, 2), dtype=torch.int32, device=dev),
+                    miss_w=torch.empty(cap, dtype=torch.float32, device=dev), miss_cap=cap,
+                    miss_count=torch.zeros(depth, dtype=torch.int32, device=dev))
 
     def stack(i):
         return [layers[(i * depth + j) % nrot] for j in range(depth)]
 
-    def step(i, events=None, route_outs=None):
-        brx.forward(sh, stack(i), xs[i % n_in], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
-                    route_outs=route_outs, events=events, stream=stream)
+    def step(i, events=None, route_outs=None, call=None):
+        for c in (range(calls) if call is None else [call]):
+            brx.forward(sh, stack(i), xs[(i * calls + c) % n_in], brx.X_BF16, T, y, ws, ws_bytes, resid_out=resid,
+                        route_outs=route_outs, events=events, stream=stream, **miss)
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -172,7 +188,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
-    tokens_per_s = T * args.steps / (total_ms / 1e3)
+    tokens_per_s = T * calls * args.steps / (total_ms / 1e3)
 
     # ---- per-kernel durations: library-recorded HIP events around each kernel, same steps
     # (every layer of a stack: the i-th kernel group of layer l is group l*nk + i)
@@ -180,13 +196,13 @@ def main():
     kern_us = {n: [] for n in names}
     if not args.profile_only:
         hip = _Hip()
-        ev_steps = min(args.steps, max(1, 20000 // (2 * nk * depth)))
-        evs = [[hip.event() for _ in range(2 * nk * depth)] for _ in range(ev_steps)]
+        ev_calls = min(args.steps * calls, max(1, 20000 // (2 * nk * depth)))
+        evs = [[hip.event() for _ in range(2 * nk * depth)] for _ in range(ev_calls)]
         torch.cuda.synchronize()
-        for j, i in enumerate(range(args.warmup, args.warmup + ev_steps)):
-            step(i, events=evs[j])
+        for j in range(ev_calls):   # one forward call per event set
+            step(args.warmup + j // calls, events=evs[j], call=j % calls)
         torch.cuda.synchronize()
-        for j in range(ev_steps):
+        for j in range(ev_calls):
             for g in range(nk * depth):
                 kern_us[names[g % nk]].append(hip.elapsed_ms(evs[j][2 * g], evs[j][2 * g + 1]) * 1e3)
         for row in evs:
@@ -229,6 +245,37 @@ def main():
             if roof:
                 roof["distinct_experts_per_layer"] = round(n_exp - 1, 2)
         dtype = "int4-dot/fp32"
+    elif args.workload == "zipf_prefill":
+        # routing of every chunk, read back once: resident picks (the only
+        # routed pairs computed), misses and per-expert load
+        res_bits = np.unpackbits(mask_np.view(np.uint8), bitorder="little")[:E].astype(bool)
+        hits, loads = [], []
+        for c in range(calls):
+            ro = [{"topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+                   "counts": torch.empty(E, dtype=torch.int32, device=dev)}]
+            step(args.warmup, route_outs=ro, call=c)
+            torch.cuda.synchronize()
+            idx = ro[0]["topk_idx"].cpu().numpy()
+            cnt = ro[0]["counts"].cpu().numpy()
+            hits.append(int(res_bits[idx].sum()))
+            loads.append(float(cnt.max()) / (T * k / E))
+        # useful gate+up flops of the resident routed and the T shared token-expert pairs, per launch
+        flops = 2.0 * (float(np.mean(hits)) + T) * d * (2 * f)
+        if dom_us:
+            achieved = flops / (dom_us * 1e-6) / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": _traffic_from_profiles(args.workload), "algorithmic_flops": flops,
+                    "avg_us": round(dom_us, 3)}
+        n_res = int(res_bits.sum())
+        layer_bytes_alg = (n_res + 1) * 3 * per_mat_codes + E * d * 4 + T * d * 2 + T * d * 4
+        metric = "MoE-layer tokens/s (32K-token Zipf-skewed prefill, 165-expert resident mask, 3-bit layer)"
+        wl = (f"Zipf(1.1) prefill: 32768 tokens in {calls} chunks of {T}, E=512 top-10 + 1 shared, d=2048, f=768, "
+              f"3-bit blocks, {n_res} resident experts")
+        dtype = "bf16-mfma/fp32"
+        zipf_stats = {"hit_rate": round(sum(hits) / (calls * T * k), 4),
+                      "misses_per_chunk": round(T * k - float(np.mean(hits)), 1),
+                      "max_over_mean_load": round(float(np.max(loads)), 2)}
     else:
         # useful gate+up flops of the T*k routed and T shared token-expert pairs
         flops = 2.0 * (T * k + T) * d * (2 * f)
@@ -245,7 +292,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
-        cpu = _cpu_baseline(w, args.cpu_sample_s)
+        cpu = _cpu_baseline(w, args.cpu_sample_s, bias=None if bias is None else bias.cpu().numpy(), mask=mask_np)
 
     rec = {
         "metric": metric,
@@ -260,14 +307,16 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl, "tokens_per_step": T, "layers_per_step": depth, "resident_layers_rotated": nrot,
-                   "parallelism": "single GPU"},
+        "config": {"workload": wl, "tokens_per_step": T * calls, "layers_per_step": depth,
+                   "resident_layers_rotated": nrot, "parallelism": "single GPU"},
         "roofline": roof,
-        "layer_hbm_frac": round(depth * layer_bytes_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_hbm_frac": round(depth * calls * layer_bytes_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {n: (round(v, 3) if v is not None else None) for n, v in kern_avg.items()},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
+    if args.workload == "zipf_prefill":
+        rec["routing"] = zipf_stats
     print(json.dumps(rec))
 
 
@@ -372,7 +421,7 @@ def traffic_summary(args):
     print(json.dumps(rec))
 
 
-def _cpu_baseline(w, target_s):
+def _cpu_baseline(w, target_s, bias=None, mask=None):
     """The oracle (grouped evaluation: each needed expert dequantised once,
     then its tokens) on a bounded sample of the workload's tokens, for about
     target_s seconds.  Calls carry one token (T = 1 and the prefill chunk) or
@@ -390,7 +439,7 @@ def _cpu_baseline(w, target_s):
     t0 = time.time()
     while n < 64:
         oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, xs[n * tc:(n + 1) * tc], Wr, codes,
-                         scales, grouped=True)
+                         scales, bias=bias, mask=mask, grouped=True)
         n += 1
         if time.time() - t0 >= target_s:
             break
