@@ -396,10 +396,22 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(LayerArgs a, int nb, i
     __shared__ int tmp[16];
     const int th = threadIdx.x, E = a.E, T = a.T;
     const int64_t n = (int64_t)T * a.k;
+    // up to SCAN_REG count blocks (T <= 4096): every count is requested at
+    // once and kept in registers for the rewrite below (one memory round trip)
+    constexpr int SCAN_REG = 64;
+    const bool inreg = nb <= SCAN_REG;
+    int v[SCAN_REG];
     int c = 0;
     if (th < E) {
-#pragma unroll 8
-        for (int b = 0; b < nb; ++b) c += a.bcnt[(int64_t)b * E + th];
+        if (inreg) {
+#pragma unroll
+            for (int b = 0; b < SCAN_REG; ++b) v[b] = b < nb ? a.bcnt[(int64_t)b * E + th] : 0;
+#pragma unroll
+            for (int b = 0; b < SCAN_REG; ++b) c += v[b];
+        } else {
+#pragma unroll 16
+            for (int b = 0; b < nb; ++b) c += a.bcnt[(int64_t)b * E + th];
+        }
     }
     int tot;
     const int off = block_excl_scan(c, tmp, &tot);
@@ -408,12 +420,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(LayerArgs a, int nb, i
         a.offsets[th] = off;
         if (a.u_counts) a.u_counts[th] = c;
         if (a.u_offsets) a.u_offsets[th] = off;
-        int run = off;
+        int run = off;   // in place: count -> first slot of the block
+        if (inreg) {
+#pragma unroll
+            for (int b = 0; b < SCAN_REG; ++b) {
+                if (b < nb) a.bcnt[(int64_t)b * E + th] = run;
+                run += v[b];
+            }
+        } else {
 #pragma unroll 8
-        for (int b = 0; b < nb; ++b) {   // in place: count -> first slot of the block
-            const int v = a.bcnt[(int64_t)b * E + th];
-            a.bcnt[(int64_t)b * E + th] = run;
-            run += v;
+            for (int b = 0; b < nb; ++b) {
+                const int cb = a.bcnt[(int64_t)b * E + th];
+                a.bcnt[(int64_t)b * E + th] = run;
+                run += cb;
+            }
         }
     }
     if (th == 0) {
