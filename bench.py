@@ -49,7 +49,7 @@ CSRC = os.path.join(ROOT, "bit_routed_expert_amd", "csrc")
 # Per workload: the dominant kernel (library kernel name and the symbol
 # rocprofv3 reports) and the source files that define it.
 WORKLOADS = {
-    "decode": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=16, inputs=None,
+    "decode": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_small_kernel", rotate=48, inputs=None,
                    sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
     "mtp_verify": dict(kernel="route_gemv_gateup", symbol="gemv_gateup_multi_kernel", rotate=48, inputs=4,
                        sources=["common.hpp", "routing.hpp", "gemv_impl.hpp", "gemv_gu3.hip"]),
