@@ -88,53 +88,21 @@ constexpr int UPL_MAX = 8;
 template <int BITS, int UPLM = UPL_MAX> struct UTile {   // UPLM: capacity (upl <= UPLM)
     uint32_t w[UPLM][Fmt<BITS>::UB / 4];
     uint32_t sc[UPLM];
-
-    __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, const uint16_t *__restrict__ msc, int in,
-                                         int row0, int R, int upl) {
-        const int lane = threadIdx.x & 63;
-        const int r = row0 + lane % R, U0 = (lane / R) * upl;
-        constexpr int UB = Fmt<BITS>::UB;
-        const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
-        if (upl % 4 == 0) {   // aligned groups: 48 or 32 contiguous bytes each
-#pragma unroll
-            for (int gq = 0; gq < UPLM / 4; ++gq) {
-                if (4 * gq < upl) {
-                    const uint4 *p = (const uint4 *)(mat + rbase + (int64_t)((U0 >> 2) + gq) * 64 * UB);
-#pragma unroll
-                    for (int i = 0; i < UB / 4; ++i) {
-                        const uint4 v = p[i];
-                        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            w[4 * gq + (4 * i + c) / (UB / 4)][(4 * i + c) % (UB / 4)] = q[c];
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < UPLM; ++u) {
-                if (u < upl) {
-                    const int U = U0 + u;
-                    const uint32_t *p = (const uint32_t *)(mat + rbase + ((int64_t)(U >> 2) * 64 + (U & 3)) * UB);
-#pragma unroll
-                    for (int i = 0; i < UB / 4; ++i) w[u][i] = p[i];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UPLM; ++u)
-            if (u < upl) sc[u] = msc[((int64_t)r * in + 32 * (U0 + u)) >> 8];
-    }
 };
 
-// A UTile filled with every load issued unconditionally (units past upl
-// re-read the lane's first unit, from cache), so filling it takes no
+// A UTile filled with every code load issued unconditionally (units past
+// upl re-read the lane's first unit, from cache), so filling it takes no
 // branches and a prefetch into it needs no wait until its values are read.
+// Scales are loaded only for the units utile_compute reads them at: the
+// last unit of each flush period (`period`, as passed to utile_compute; a
+// period never spans two weight blocks) and the lane's last unit; with a
+// period of one unit every scale is read and the loads stay unconditional.
 // GROUPED: upl is a multiple of 4 (16-byte group loads).
 // r: this lane's row, U0: its first unit.
 template <int BITS, bool GROUPED, int UPLM = UPL_MAX>
 __device__ __forceinline__ void utile_load_all(UTile<BITS, UPLM> &t, const uint8_t *__restrict__ mat,
-                                               const uint16_t *__restrict__ msc, int in, int r, int U0, int upl) {
+                                               const uint16_t *__restrict__ msc, int in, int r, int U0, int upl,
+                                               int period) {
     constexpr int UB = Fmt<BITS>::UB;
     const int64_t rbase = ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
     if constexpr (GROUPED) {
@@ -159,8 +127,15 @@ __device__ __forceinline__ void utile_load_all(UTile<BITS, UPLM> &t, const uint8
             for (int i = 0; i < UB / 4; ++i) t.w[u][i] = p[i];
         }
     }
+    if (period == 1) {   // every unit's scale is read: unconditional, like the codes
 #pragma unroll
-    for (int u = 0; u < UPLM; ++u) t.sc[u] = msc[((int64_t)r * in + 32 * (U0 + (u < upl ? u : 0))) >> 8];
+        for (int u = 0; u < UPLM; ++u) t.sc[u] = msc[((int64_t)r * in + 32 * (U0 + (u < upl ? u : 0))) >> 8];
+    } else {
+#pragma unroll
+        for (int u = 0; u < UPLM; ++u)
+            if (u < upl && (u == upl - 1 || (U0 + u + 1) % period == 0))
+                t.sc[u] = msc[((int64_t)r * in + 32 * (U0 + u)) >> 8];
+    }
 }
 
 // Row sums of a UTile against NT tokens (digit planes in LDS at dig +
@@ -346,9 +321,11 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     UTile<BITS> wt;
     const int r = row0 + lane % R, U0 = (lane / R) * upl;
     if (upl % 4 == 0)
-        utile_load_all<BITS, true>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl);
+        utile_load_all<BITS, true>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl,
+                                   unit_period(d, XGROUP_UNITS));
     else
-        utile_load_all<BITS, false>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl);
+        utile_load_all<BITS, false>(wt, a.codes + mi * mat_bytes, a.scales + mi * mat_blocks, d, r, U0, upl,
+                                    unit_period(d, XGROUP_UNITS));
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_s_barrier();         // every wave's staged digit planes and sums visible
     float res[NT];
@@ -505,12 +482,13 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     int job = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (threadIdx.x >> 6));
     if (job >= njobs) return;
     const int lane = threadIdx.x & 63, rl = lane % R, m = rl >= half ? 1 : 0, U0 = (lane / R) * upl;
+    const int uper = unit_period(a.d, XGROUP_UNITS);
     const size_t mat_bytes = (size_t)a.d * a.f * BITS / 8, mat_blocks = (size_t)a.d * a.f / 256;
     // this lane's row of the job's expert: gate (m = 0) or up (m = 1) row c0 + rl - m*half
 #define GU_LOAD(T_, IT_, JOB_)                                                                                         \
     utile_load_all<BITS, GROUPED>(T_, a.codes + ((size_t)(IT_).expert * 3 + m) * mat_bytes,                           \
                                   a.scales + ((size_t)(IT_).expert * 3 + m) * mat_blocks, a.d,                         \
-                                  ((JOB_) % groups) * half + rl - m * half, U0, upl)
+                                  ((JOB_) % groups) * half + rl - m * half, U0, upl, uper)
     WorkItem it;
     uint32_t tpk;
     {
@@ -656,7 +634,7 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
         UTile<BITS, UPLM> wt;   // loads issued unconditionally: the waits that follow cover only what they need
         utile_load_all<BITS, UPLM % 4 == 0, UPLM>(wt, a.codes + ((size_t)it.expert * 3 + 2) * ((size_t)d * f * BITS / 8),
                                                   a.scales + ((size_t)it.expert * 3 + 2) * ((size_t)d * f / 256), f,
-                                                  row0 + lane % R, (lane / R) * upl, upl);
+                                                  row0 + lane % R, (lane / R) * upl, upl, 1);
         st.store(a, upl, dstride, wdig, wsum, wscl);
         float res[1];
         utile_compute<BITS, 1, UPLM>(wt, R, upl, 1, wdig, dstride, wsum, units, wscl, units, HGROUP_UNITS,
@@ -746,9 +724,9 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
     for (int q = 0; q < DN_QMAX; ++q) {
         const int r = row0 + (q < Q ? q : 0) * R + lane % R;
         if constexpr (UPLM % 4 == 0)
-            utile_load_all<BITS, true, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl);
+            utile_load_all<BITS, true, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl, 1);
         else
-            utile_load_all<BITS, false, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl);
+            utile_load_all<BITS, false, UPLM>(wt[q], mcodes, mscl, f, r, (lane / R) * upl, upl, 1);
     }
     const int dstride = units * XPLANES * 4 + S * 4;
     uint32_t *dig = lds;
