@@ -345,14 +345,15 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
     }
 }
 
-// One token: blocks of 2 waves, R columns of h each.  The first f/R
-// blocks take the shared expert and need no routing; every other group of
-// f/R blocks takes one pick: each block takes the top-k itself from the
-// router logits (a few KB, one wave) while the other wave stages the input
-// digit planes, unit sums and group scales, and runs its pick's rows; the
-// last block writes the routing outputs and the work list instead.
+// One token: blocks of G gate waves and G up waves, G*R columns of h each
+// (G = 2 when f allows).  The first f/(G*R) blocks take the shared expert
+// and need no routing; every other group of f/(G*R) blocks takes one pick:
+// each block takes the top-k itself from the router logits (a few KB, one
+// wave) while the other waves stage the input digit planes, unit sums and
+// group scales, and runs its pick's rows; the last block writes the routing
+// outputs and the work list instead.
 template <int BITS>
-__global__ __launch_bounds__(128) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
+__global__ __launch_bounds__(256) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
     const GuLds g(lds, a.d, R, a.T, 1);
     const SmallRoute L(lds + route_off, a.E);
@@ -780,14 +781,18 @@ inline bool gemv_supported_impl(int d, int f, int bits) {
 // a launch that would need more is refused rather than attempted.
 constexpr size_t LDS_LIMIT = 64 * 1024;
 
-// One token: 2-wave blocks of R columns of h per work item, plus the
-// routing writer.
+// One token: blocks of G gate + G up waves (G*R columns of h) per work
+// item, plus the routing writer.  Two wave pairs per block halve the input
+// staging and the top-k waves per column (measured faster than one pair and
+// than four).
 template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int R = 64 / unit_slices(a.d, 8);
+    const int G = a.f % (2 * R) == 0 ? 2 : 1;   // the result area holds up to four wave pairs' rows
     const int off = gateup_lds_words(a.d, R, 1, 1);
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
     if (a.T != 1 || lds > LDS_LIMIT) return hipErrorInvalidValue;
-    STRATA_LAUNCH(gemv_gateup_small_kernel<BITS>, dim3(max_items * (a.f / R) + 1), dim3(128), lds, s, a, R, off);
+    STRATA_LAUNCH(gemv_gateup_small_kernel<BITS>, dim3(max_items * (a.f / (G * R)) + 1), dim3(128 * G), lds, s, a,
+                  R, off);
     return hipGetLastError();
 }
 
