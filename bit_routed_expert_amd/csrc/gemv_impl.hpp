@@ -662,15 +662,15 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
 }
 
 // Any T <= 8 (the path for T >= 2): block = one work item (<= 2 slots) x
-// 128 rows of Wd (4 waves, Q = 32/R tiles of R rows each, every tile's
-// codes requested at once).  The item's h rows are quantised into LDS
+// 64 rows of Wd (4 waves, Q = 16/R tiles of R rows each, every tile's codes
+// requested at once; 64-row blocks measured faster than 128 and 32).  The item's h rows are quantised into LDS
 // while the codes load, exactly as the one-token kernel quantises them
 // (per 32-column unit: exponent from the unit's max |h|, 6 balanced base-16
 // digit planes, digit sum, 2^-E; the 4 chunks of a unit in 4 neighbouring
 // lanes), and shared by the waves; expert outputs go to Y and the combine
 // kernel sums them.  Per (slot, row) the arithmetic is the one-token
 // kernel's, so results do not depend on T.
-constexpr int DN_WAVES = 4, DN_QMAX = 4;   // Q = 128 / (4 R): blocks own 128 rows
+constexpr int DN_WAVES = 4, DN_ROWS = 64, DN_QMAX = 2;   // Q = DN_ROWS / (4 R) <= 2 (R >= 8)
 
 __host__ __device__ inline int down_multi_lds_words(int f, int R) {
     const int S = 64 / R, units = f / 32;
@@ -813,11 +813,12 @@ template <int BITS> hipError_t gateup_multi_launch(const LayerArgs &a, int max_i
 }
 
 template <int BITS> hipError_t down_multi_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / unit_slices(a.f, 8), Q = 128 / (DN_WAVES * R);
+    const int R = 64 / unit_slices(a.f, 8), Q = DN_ROWS / (DN_WAVES * R);
     const size_t lds = 4 * (size_t)down_multi_lds_words(a.f, R);
     const int upl = (a.f / 32) / (64 / R);
-    if (Q < 1 || Q > DN_QMAX || a.d % 128 || lds > LDS_LIMIT) return hipErrorInvalidValue;
-    const dim3 grid(max_items * (a.d / 128)), block(64 * DN_WAVES);
+    if (Q < 1 || Q > DN_QMAX || Q * DN_WAVES * R != DN_ROWS || a.d % DN_ROWS || lds > LDS_LIMIT)
+        return hipErrorInvalidValue;
+    const dim3 grid(max_items * (a.d / DN_ROWS)), block(64 * DN_WAVES);
     if (upl == 3)   // d_ff = 768: 3 units per lane
         STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 3>), grid, block, lds, s, a, R, Q);
     else if (upl == 1)
