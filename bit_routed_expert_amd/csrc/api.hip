@@ -29,7 +29,7 @@ constexpr int SMALL_T = 8;
 
 struct Layout {
     size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf,
-        wp, xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
+        xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -70,7 +70,6 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.xsum = take(4 * Tq * (d / 32));
     l.xscl = take(4 * Tq * ((d + 255) / 256));
     l.hf = take(4 * Sq * f);
-    l.wp = take(sp ? 0 : (size_t)3 * E * d * 2);
     l.xa = take((size_t)2 * Tg * d * 2);
     l.sx = take(4 * Tg * (d / 128));
     l.ha = take((size_t)2 * Sg * f * 2);
@@ -123,7 +122,6 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xscl = (float *)(ws + l.xscl);
     a.hf = (float *)(ws + l.hf);
     a.Y = (float *)(ws + l.Y);
-    a.wp = (uint16_t *)(ws + l.wp);
     a.xa = (uint16_t *)(ws + l.xa);
     a.sx = (float *)(ws + l.sx);
     a.ha = (uint16_t *)(ws + l.ha);

@@ -170,7 +170,6 @@ struct LayerArgs {
     float *Y;            // [slots][d] expert outputs (larger T)
     // GEMM path: bf16 hi/lo activations, columns permuted inside each
     // 128-column step, and their sums over each step (x) or 32-feature group (h)
-    uint16_t *wp;        // [3][E][d] exact bf16 pieces of Wr (GEMM-path router)
     uint16_t *xa;        // [2][T][d]
     float *sx;           // [T][d/128]
     uint16_t *ha;        // [2][slots][f]

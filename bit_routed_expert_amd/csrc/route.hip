@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
 
 // Router dot products x[t] . Wr[e] on the bf16 matrix cores (the logit is
 // inv_rms[t] times this plus bias[e], formed by the top-k kernel).  Wr (fp32)
-// is split into three bf16 pieces, exactly, once per call
-// (route_split_kernel); x is one piece when it is bf16, else three (products
+// is split into three exact bf16 pieces as it is staged into LDS; x is one
+// piece when it is bf16, else three (products
 // of pieces below 2^-32 of the leading one are dropped).  Every product is
 // exact in fp32; each 256-column block is summed on its own and the block
 // sums are added in order.  The columns are cut into zsplit equal ranges of
@@ -187,26 +187,6 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
 // planes in order.  Block tile 128 tokens x 64 experts; wave w owns tokens
 // 32*w .. +32 against all 64 experts (two 32x32 MFMA tiles).
 constexpr int RT_T = 128, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
-
-// Wr as three exact bf16 pieces, once per call: wp[q][e][i], Wr = hi + mid + lo.
-__global__ __launch_bounds__(256) void route_split_kernel(LayerArgs a) {
-    const int64_t n8 = (int64_t)a.E * a.d / 8, c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= n8) return;
-    const float4 *src = (const float4 *)(a.Wr + 8 * c);
-    const float4 w0 = src[0], w1 = src[1];
-    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    uint16_t hw[3][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) split3(w[j], hw[0][j], hw[1][j], hw[2][j]);
-    const int64_t plane = (int64_t)a.E * a.d;
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        uint32_t u[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = (uint32_t)hw[q][2 * j] | ((uint32_t)hw[q][2 * j + 1] << 16);
-        *(uint4 *)(a.wp + q * plane + 8 * c) = make_uint4(u[0], u[1], u[2], u[3]);
-    }
-}
 
 template <int PX>
 __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel(LayerArgs a) {
@@ -230,10 +210,10 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
     const int xr = th >> 1, xc = (th & 1) * 16;
     const int wr = th >> 2, wc = (th & 3) * 8;
     const int64_t xoff = (int64_t)min(t0 + xr, T - 1) * d + xc;
-    const int64_t woff = (int64_t)min(e0 + wr, E - 1) * d + wc, plane = (int64_t)E * d;
+    const int64_t woff = (int64_t)min(e0 + wr, E - 1) * d + wc;
     const bool wvalid = e0 + wr < E;
     float xv[16];
-    uint4 wq[3];   // 8 columns of this thread's Wr row as three bf16 pieces
+    float4 wf[2];   // 8 columns of this thread's Wr row (fp32)
     auto load = [&](int k0) __attribute__((always_inline)) {
         if (a.x_is_bf16) {
             const uint4 *p = (const uint4 *)((const uint16_t *)a.x + xoff + k0);
@@ -252,8 +232,9 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
                 xv[4 * j] = q.x; xv[4 * j + 1] = q.y; xv[4 * j + 2] = q.z; xv[4 * j + 3] = q.w;
             }
         }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) wq[q] = *(const uint4 *)(a.wp + q * plane + woff + k0);
+        const float4 *pw = (const float4 *)(a.Wr + woff + k0);
+        wf[0] = pw[0];
+        wf[1] = pw[1];
     };
     f32x16_t P[2], acc[2];
 #pragma unroll
@@ -263,7 +244,20 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
     load(kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += RT_K) {
         __syncthreads();
-        {   // pieces into LDS
+        {   // pieces into LDS: Wr = hi + mid + lo exactly, two columns packed per word
+            const float w[8] = {wf[0].x, wf[0].y, wf[0].z, wf[0].w, wf[1].x, wf[1].y, wf[1].z, wf[1].w};
+            uint32_t u[3][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint16_t a0, b0, c0, a1, b1, c1;
+                split3(w[2 * j], a0, b0, c0);
+                split3(w[2 * j + 1], a1, b1, c1);
+                u[0][j] = wvalid ? ((uint32_t)a0 | ((uint32_t)a1 << 16)) : 0u;
+                u[1][j] = wvalid ? ((uint32_t)b0 | ((uint32_t)b1 << 16)) : 0u;
+                u[2][j] = wvalid ? ((uint32_t)c0 | ((uint32_t)c1 << 16)) : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) *(uint4 *)(ws[q] + wr * RT_RS + wc) = make_uint4(u[q][0], u[q][1], u[q][2], u[q][3]);
             uint16_t hx[PX][16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -279,9 +273,6 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
                 dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
                 dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
             }
-#pragma unroll
-            for (int q = 0; q < 3; ++q)
-                *(uint4 *)(ws[q] + wr * RT_RS + wc) = wvalid ? wq[q] : make_uint4(0u, 0u, 0u, 0u);
         }
         __syncthreads();
         if (k0 + RT_K < kend) load(k0 + RT_K);
@@ -538,8 +529,6 @@ int route_logit_splits(int d) {
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
     const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T, a.zsplit);
     if (a.d % RT_K || a.zsplit < 1 || a.d % a.zsplit || (a.d / a.zsplit) % RT_K || a.E > 1024) return hipErrorInvalidValue;
-    const int64_t n8 = (int64_t)a.E * a.d / 8;
-    STRATA_LAUNCH(route_split_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a);
     if (a.x_is_bf16)
         STRATA_LAUNCH(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
     else
