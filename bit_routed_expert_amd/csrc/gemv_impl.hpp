@@ -662,15 +662,17 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
 }
 
 // Any T <= 8 (the path for T >= 2): block = one work item (<= 2 slots) x
-// 64 rows of Wd (4 waves, Q = 16/R tiles of R rows each, every tile's codes
-// requested at once; 64-row blocks measured faster than 128 and 32).  The item's h rows are quantised into LDS
+// 8R rows of Wd (8 waves, one tile of R rows each, every tile's codes
+// requested at once; 64-row blocks of 8 waves measured faster than 64 rows
+// of 4 waves, 128 rows and 32 rows).  The item's h rows are quantised into LDS
 // while the codes load, exactly as the one-token kernel quantises them
 // (per 32-column unit: exponent from the unit's max |h|, 6 balanced base-16
 // digit planes, digit sum, 2^-E; the 4 chunks of a unit in 4 neighbouring
 // lanes), and shared by the waves; expert outputs go to Y and the combine
 // kernel sums them.  Per (slot, row) the arithmetic is the one-token
 // kernel's, so results do not depend on T.
-constexpr int DN_WAVES = 4, DN_ROWS = 64, DN_QMAX = 2;   // Q = DN_ROWS / (4 R) <= 2 (R >= 8)
+constexpr int DN_WAVES = 8, DN_QMAX = 1;   // Q = 1 tile of R rows per wave
+constexpr int DN_THREADS = 64 * DN_WAVES;
 
 __host__ __device__ inline int down_multi_lds_words(int f, int R) {
     const int S = 64 / R, units = f / 32;
@@ -696,7 +698,7 @@ __device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkI
 }
 
 template <int BITS, int UPLM>
-__global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R, int Q) {
+__global__ __launch_bounds__(DN_THREADS) void gemv_down_multi_kernel(LayerArgs a, int R, int Q) {
     extern __shared__ uint32_t lds[];
     const int th = threadIdx.x, wave = th >> 6, lane = th & 63;
     const int d = a.d, f = a.f, units = f / 32, S = 64 / R, upl = units / S;
@@ -708,11 +710,11 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
     // loads in the order they are used: this thread's h chunk, then the code
     // tiles (all unconditional, so each wait covers only what it needs)
     const int cps = f / 8, nch = it.ntok * cps;   // 8-column chunks of the item's h rows
-    constexpr int HPER = (ITEM_TOK * MAX_HUNITS * 4 + 255) / 256;   // chunks per thread
+    constexpr int HPER = (ITEM_TOK * MAX_HUNITS * 4 + DN_THREADS - 1) / DN_THREADS;   // chunks per thread
     float4 hv[2 * HPER];
 #pragma unroll
     for (int u = 0; u < HPER; ++u) {
-        const int cc = min(th + 256 * u, nch - 1);
+        const int cc = min(th + DN_THREADS * u, nch - 1);
         const float4 *src = (const float4 *)(a.hf + (size_t)it.slot0 * f) + 2 * cc;
         hv[2 * u] = src[0];
         hv[2 * u + 1] = src[1];
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(256) void gemv_down_multi_kernel(LayerArgs a, int R
     // the 4 chunks of a unit sit in 4 neighbouring lanes
 #pragma unroll
     for (int u = 0; u < HPER; ++u) {
-        const int c = th + 256 * u;
+        const int c = th + DN_THREADS * u;
         const float h[8] = {hv[2 * u].x, hv[2 * u].y, hv[2 * u].z, hv[2 * u].w,
                             hv[2 * u + 1].x, hv[2 * u + 1].y, hv[2 * u + 1].z, hv[2 * u + 1].w};
         float mx = 0.f;
@@ -813,12 +815,11 @@ template <int BITS> hipError_t gateup_multi_launch(const LayerArgs &a, int max_i
 }
 
 template <int BITS> hipError_t down_multi_launch(const LayerArgs &a, int max_items, hipStream_t s) {
-    const int R = 64 / unit_slices(a.f, 8), Q = DN_ROWS / (DN_WAVES * R);
+    const int R = 64 / unit_slices(a.f, 8), Q = 1, rows = DN_WAVES * Q * R;
     const size_t lds = 4 * (size_t)down_multi_lds_words(a.f, R);
     const int upl = (a.f / 32) / (64 / R);
-    if (Q < 1 || Q > DN_QMAX || Q * DN_WAVES * R != DN_ROWS || a.d % DN_ROWS || lds > LDS_LIMIT)
-        return hipErrorInvalidValue;
-    const dim3 grid(max_items * (a.d / DN_ROWS)), block(64 * DN_WAVES);
+    if (Q > DN_QMAX || a.d % rows || lds > LDS_LIMIT) return hipErrorInvalidValue;
+    const dim3 grid(max_items * (a.d / rows)), block(DN_THREADS);
     if (upl == 3)   // d_ff = 768: 3 units per lane
         STRATA_LAUNCH((gemv_down_multi_kernel<BITS, 3>), grid, block, lds, s, a, R, Q);
     else if (upl == 1)
