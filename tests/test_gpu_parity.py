@@ -96,6 +96,25 @@ def test_verify_batch_five_tokens_and_batch_invariance():
         np.testing.assert_array_equal(one["y"][0], got["y"][t])
 
 
+@pytest.mark.parametrize("T", [2, 6, 8])
+def test_full_size_batches_match_oracle_and_single_tokens(T):
+    """Other T <= 8 batch sizes on the full-size layer (T = 8: 80 picks):
+    routing bit-exact, outputs against the oracle, and each token's row equal
+    to its own one-token call bit for bit."""
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 0)
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=11 + T)
+    print(f"case full-size T={T}", flush=True)
+    ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
+    dl = [G.layer_to_dev(L)]
+    got = G.run_forward(w, dl, G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+    for t in range(T):
+        one = G.run_forward(w, dl, G.dev(x[t:t + 1]), 0, 1, want_route=False)
+        np.testing.assert_array_equal(one["y"][0], got["y"][t])
+
+
 def test_decode_repeat_is_bitwise_identical():
     w, L, x, T = _layer_case("decode", rep=5)
     dl = [G.layer_to_dev(L)]
