@@ -61,18 +61,20 @@ def test_tiny_layer_with_mask_and_misses():
     assert np.max(np.abs(got["miss_w"][0][:n] - ref["miss_w"]), initial=0) <= G.GATE_TOL
 
 
-@pytest.mark.parametrize("name,rep", [("tiny", 0), ("tiny", 3), ("decode", 0), ("decode", 4)])
-def test_one_token_with_resident_mask(name, rep):
-    """The one-token kernels with a resident mask: non-resident picks are
-    skipped in gate/up and in the in-block combine, and listed as misses."""
+@pytest.mark.parametrize("name,T,rep", [("tiny", 1, 0), ("tiny", 1, 3), ("decode", 1, 0), ("decode", 1, 4),
+                                        ("decode", 5, 2), ("decode", 8, 5)])
+def test_decode_path_with_resident_mask(name, T, rep):
+    """The T <= 8 kernels with a resident mask (one-token kernels at T = 1):
+    non-resident picks are skipped in gate/up, down and the combine, and
+    listed as misses."""
     w = synth.WORKLOADS[name]
     nw = (w.n_experts + 31) // 32
     bits = np.random.default_rng(100 + rep).random(w.n_experts) < 0.5   # about half resident
     mask = np.zeros(nw, np.uint32)
     for e in np.nonzero(bits)[0]:
         mask[e // 32] |= np.uint32(1) << np.uint32(e % 32)
-    w, L, x, T = _layer_case(name, T=1, rep=rep, with_mask=mask)
-    print(f"case {name} T=1 masked rep={rep}", flush=True)
+    w, L, x, T = _layer_case(name, T=T, rep=rep, with_mask=mask)
+    print(f"case {name} T={T} masked rep={rep}", flush=True)
     ref = _oracle_layer(w, L, synth.bf16_to_f32(x))
     got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
     G.assert_route_equal(got["route"][0], ref)
