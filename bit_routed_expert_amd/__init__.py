@@ -36,7 +36,7 @@ class Shape(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("codes", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("resident_mask", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("resident_mask", ctypes.c_void_p), ("bits", ctypes.c_int32)]
 
 
 class RouteOut(ctypes.Structure):
@@ -110,10 +110,11 @@ class LayerData:
     scales: object
     router_bias: object = None
     resident_mask: object = None
+    bits: int = 0   # this layer's code width (3 or 2); 0 = the shape's
 
     def as_c(self) -> Layer:
         return Layer(_ptr(self.router_w), _ptr(self.router_bias), _ptr(self.codes), _ptr(self.scales),
-                     _ptr(self.resident_mask))
+                     _ptr(self.resident_mask), int(self.bits))
 
 
 def shape(n_experts: int, top_k: int, d_model: int, d_ff: int, bits: int, n_shared: int = 1) -> Shape:

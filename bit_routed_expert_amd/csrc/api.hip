@@ -259,6 +259,7 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
     for (int l = 0; l < L; ++l) {
         if (!layers[l].router_w || !layers[l].codes || !layers[l].scales) return STRATA_EINVAL;
         if (!aligned16(layers[l].router_w) || !aligned16(layers[l].codes)) return STRATA_EINVAL;
+        if (layers[l].bits != 0 && layers[l].bits != 3 && layers[l].bits != 2) return STRATA_EUNSUPPORTED;
         any_mask |= layers[l].resident_mask != nullptr;
     }
     if (any_mask && (!miss_te || !miss_w || !miss_count)) return STRATA_EINVAL;
@@ -276,6 +277,7 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         a.codes = ly.codes;
         a.scales = ly.scales;
         a.mask = ly.resident_mask;
+        a.bits = ly.bits ? ly.bits : shape->bits;   // the workspace layout does not depend on it
         if (l == 0) {
             a.x = x;
             a.x_is_bf16 = xdtype == STRATA_X_BF16;

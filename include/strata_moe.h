@@ -96,6 +96,10 @@ typedef struct {
     const uint8_t *codes;           /* (E+1) experts, format above */
     const uint16_t *scales;         /* (E+1) experts, fp16 bit patterns */
     const uint32_t *resident_mask;  /* [ceil(E/32)] bitset (bit e%32 of word e/32), or NULL = all resident */
+    int32_t bits;                   /* this layer's code width, 3 or 2 (codes and scales in that format),
+                                       or 0 = the shape's bits.  Layers of one stack may differ: precision
+                                       can change from layer to layer (greenbean-ai, "Strata 如何讓 12GB 顯卡跑
+                                       Qwen3.8-Flash-Next？", §四).  Any other value: STRATA_EUNSUPPORTED. */
 } strata_moe_layer;
 
 /* [host] struct of optional [dev] outputs (any field may be NULL):

@@ -59,6 +59,18 @@ def test_unsupported_bits():
     assert st == brx.STRATA_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("bits", [1, 4, -3])
+def test_unsupported_layer_bits(bits):
+    """A layer's own code width must be 0 (the shape's), 3 or 2."""
+    lib = brx.load_library()
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    ly = (brx.Layer * 2)(brx.Layer(0x1000, None, 0x2000, 0x3000, None, 2),
+                         brx.Layer(0x1000, None, 0x2000, 0x3000, None, bits))
+    st = lib.strata_moe_forward(ctypes.byref(sh), ly, 2, 0x4000, 0, 1, 0, 0x5000, None, None, None, None, 0, None,
+                                0x6000, 1 << 30, None, 0, None)
+    assert st == brx.STRATA_EUNSUPPORTED
+
+
 def _fake_layer():
     # non-null placeholders: validation fails before anything touches them
     return brx.Layer(0x1000, None, 0x2000, 0x3000, None)

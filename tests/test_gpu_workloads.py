@@ -220,10 +220,13 @@ def test_wide_topk_and_shared_picks(bits, T):
 
 @pytest.mark.parametrize("E,k,d,f,bits,T", [(1024, 8, 256, 128, 3, 1), (1024, 8, 256, 128, 3, 5),
                                             (1024, 8, 256, 128, 2, 20), (1000, 6, 384, 384, 3, 1),
-                                            (1000, 6, 384, 384, 2, 5), (1000, 6, 384, 384, 3, 20)])
+                                            (1000, 6, 384, 384, 2, 5), (1000, 6, 384, 384, 3, 20),
+                                            (256, 10, 2048, 768, 3, 1), (256, 10, 2048, 768, 2, 5),
+                                            (256, 10, 2048, 768, 3, 20)])
 def test_wide_expert_counts_and_odd_widths(E, k, d, f, bits, T):
     """More than 512 experts (16 logits per lane in the top-k, the largest
     supported expert count), an expert count that is not a multiple of 64,
+    the expert-pruned 256-expert full-size layer,
     and d = f = 384 (rows of 1.5 scale blocks, 12 units per row: 128-column
     scale steps on the matrix-core path) on the decode kernels (T = 1, 5)
     and the matrix-core path (T = 20)."""
@@ -236,3 +239,47 @@ def test_wide_expert_counts_and_odd_widths(E, k, d, f, bits, T):
     got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
     G.assert_route_equal(got["route"][0], ref)
     G.assert_close(got["y"], ref["out"])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 5), ("tiny", 20), ("decode", 1), ("decode", 5)])
+def test_mixed_bit_width_stack(name, T):
+    """Layers of one stack in different code widths (3-bit, 2-bit, 3-bit on
+    the small layer; 3-bit then 2-bit at full size) through one forward call
+    on the one-token, T <= 8 and matrix-core paths: every layer's routing
+    against the oracle's chain, the last output and residual within the
+    bound."""
+    import bit_routed_expert_amd as brx
+    base = synth.WORKLOADS[name]
+    wb = {3: base, 2: synth.Workload(base.name + "_b2", base.n_experts, base.top_k, base.d_model, base.d_ff, 2,
+                                     base.tokens, seed=base.seed + 0x100)}
+    widths = [3, 2, 3] if name == "tiny" else [3, 2]
+    Ls, refs = [], []
+    x0 = xl = None
+    for l, b in enumerate(widths):
+        w = wb[b]
+        attempt = 0
+        while True:
+            Lr = W.layer_data(w, l, attempt)
+            if l == 0:
+                x0, _ = W.draw_tokens(w, Lr["Wr"], None, range(T), rep=31)
+                xl = synth.bf16_to_f32(x0)
+            u = oracle.layer_input(xl, l)
+            if oracle.topk_margin(oracle.logits(u, Lr["Wr"]), w.top_k).min() >= W.MARGIN:
+                break
+            attempt += 1
+        r = oracle.moe_layer(b, w.n_experts, w.top_k, w.d_model, w.d_ff, u, Lr["Wr"], Lr["codes"], Lr["scales"])
+        Ls.append(Lr)
+        refs.append(r)
+        xl = oracle.residual_add(xl, r["out"])
+    print(f"case mixed widths {widths} {name} T={T}", flush=True)
+    dl = []
+    for Lr, b in zip(Ls, widths):
+        ld = G.layer_to_dev(Lr)
+        ld.bits = b
+        dl.append(ld)
+    got = G.run_forward(base, dl, G.dev(x0), 0, T)
+    for l, r in enumerate(refs):
+        np.testing.assert_array_equal(got["route"][l]["topk_idx"], r["idx"], err_msg=f"layer {l} ids")
+    G.assert_close(got["y"], refs[-1]["out"], what="last layer output")
+    G.assert_close(got["resid"], xl, what="residual")
+    assert isinstance(dl[1], brx.LayerData) and dl[1].bits == 2
