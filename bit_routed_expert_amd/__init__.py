@@ -69,6 +69,10 @@ def load_library(path: str = LIB_PATH):
     lib.strata_moe_forward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), i32, vp, ctypes.c_int, i32,
                                        ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32, vp, vp, sz,
                                        ctypes.POINTER(ctypes.c_void_p), i32, vp]
+    lib.strata_moe_counts_accumulate.restype = ctypes.c_int
+    lib.strata_moe_counts_accumulate.argtypes = [vp, vp, i32, vp]
+    lib.strata_moe_resident_topn.restype = ctypes.c_int
+    lib.strata_moe_resident_topn.argtypes = [vp, i32, i32, vp, vp]
     lib.strata_moe_kernel_names.restype = i32
     lib.strata_moe_kernel_names.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(ctypes.c_char_p), i32]
     lib.strata_status_str.restype = ctypes.c_char_p
@@ -78,7 +82,8 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED_SYMBOLS = ("strata_moe_workspace_bytes", "strata_moe_route", "strata_moe_forward",
-                    "strata_moe_kernel_names", "strata_status_str")
+                    "strata_moe_counts_accumulate", "strata_moe_resident_topn", "strata_moe_kernel_names",
+                    "strata_status_str")
 
 
 def _ptr(t) -> Optional[int]:
@@ -169,3 +174,14 @@ def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_la
     _check(lib.strata_moe_forward(ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last),
                                   _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w), miss_cap, _ptr(miss_count),
                                   _ptr(ws), ws_bytes, ev, n_ev, _stream(stream)))
+
+
+def counts_accumulate(counts_acc, counts, n_experts: int, stream=None):
+    """counts_acc[e] += counts[e] (int64 running totals, int32 per-call counts)."""
+    _check(load_library().strata_moe_counts_accumulate(_ptr(counts_acc), _ptr(counts), n_experts, _stream(stream)))
+
+
+def resident_topn(counts_acc, n_experts: int, n_resident: int, mask_out, stream=None):
+    """mask_out = the n_resident most-picked experts (count desc, index asc)."""
+    _check(load_library().strata_moe_resident_topn(_ptr(counts_acc), n_experts, n_resident, _ptr(mask_out),
+                                                   _stream(stream)))

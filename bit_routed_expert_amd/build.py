@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstrata_moe.so")
-SOURCES = ["api.hip", "route.hip", "gemv.hip", "gemv_gu3.hip", "gemv_gu2.hip", "gemv_dn3.hip", "gemv_dn2.hip",
+SOURCES = ["api.hip", "popularity.hip", "route.hip", "gemv.hip", "gemv_gu3.hip", "gemv_gu2.hip", "gemv_dn3.hip", "gemv_dn2.hip",
            "gemm.hip", "gemm_gu3.hip", "gemm_gu2.hip", "gemm_dn3.hip", "gemm_dn2.hip", "combine.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -152,6 +152,23 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
  * for a token count T; returns how many (<= max) and writes static strings. */
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max);
 
+/* Running expert popularity (the expert cache learns which experts are hot as
+ * it is used: wiselychen.com, technique 2 "專家快取與 CPU／GPU 分工"; wiki.nginx.tw,
+ * "Strata：把 1250 億參數的 Qwen3.8-Flash-Next 跑在遊戲顯卡上", dynamic expert cache item).
+ * counts_acc[e] += counts[e] for e < n_experts: [dev] int64 [E] running totals (caller-owned, zeroed
+ * by the caller before the first call) and [dev] int32 [E] per-call counts such as
+ * strata_route_out.counts.  Enqueued on `stream`.  EINVAL: a null pointer or E outside 1..1024;
+ * EHIP: the launch failed. */
+strata_status strata_moe_counts_accumulate(int64_t *counts_acc, const int32_t *counts, int32_t n_experts,
+                                           void *stream);
+
+/* Resident set from running counts: mask_out ([dev] uint32 [ceil(E/32)], bit e%32 of word e/32, the
+ * strata_moe_layer.resident_mask format) gets the n_resident experts with the largest counts, ties
+ * to the lower index, so the mask is the same on every run.  Enqueued on `stream`.  EINVAL: a null
+ * pointer, E outside 1..1024 or n_resident outside 0..E; EHIP: the launch failed. */
+strata_status strata_moe_resident_topn(const int64_t *counts_acc, int32_t n_experts, int32_t n_resident,
+                                       uint32_t *mask_out, void *stream);
+
 /* Static description of a status (for STRATA_EHIP, of the last HIP error). */
 const char *strata_status_str(strata_status s);
 

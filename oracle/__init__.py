@@ -229,3 +229,17 @@ def layer_input(x_l: np.ndarray, layer: int, norm_first: bool = False) -> np.nda
 def residual_add(x_l: np.ndarray, out: np.ndarray) -> np.ndarray:
     """x_{l+1} = x_l + out_l, one fp32 rounding per element."""
     return (_c(x_l, np.float32) + _c(out, np.float32)).astype(np.float32)
+
+
+def resident_topn(counts, n: int) -> np.ndarray:
+    """uint32 bitset [ceil(E/32)] of the n experts with the largest counts,
+    ties to the lower index: a stable sort of the experts by descending count
+    (the cache keeps the most-used experts: wiselychen.com, technique 2
+    "專家快取與 CPU／GPU 分工")."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.shape[0]
+    order = sorted(range(E), key=lambda e: (-int(counts[e]), e))
+    mask = np.zeros((E + 31) // 32, dtype=np.uint32)
+    for e in order[:n]:
+        mask[e // 32] |= np.uint32(1) << np.uint32(e % 32)
+    return mask

@@ -379,3 +379,21 @@ def test_zipf_targets_and_generated_popularity():
     assert np.all(np.abs(pop[ranks[:20]] - t[:20]) < 0.12)
     hit = np.isin(idx, ranks[: w.resident]).mean()
     assert 0.6 < hit < 0.99        # the pages' hit-rate band is roughly 67.8-98%
+
+
+def test_resident_topn_hand_example():
+    """Hand-worked resident sets: largest counts first, equal counts to the
+    lower index, n = 0 and n = E at the ends."""
+    counts = [5, 9, 9, 0, 7, 9, 1, 7]
+    # order by (count desc, index asc): 1, 2, 5, 4, 7, 0, 6, 3
+    assert list(oracle.resident_topn(counts, 3)) == [(1 << 1) | (1 << 2) | (1 << 5)]
+    assert list(oracle.resident_topn(counts, 4)) == [(1 << 1) | (1 << 2) | (1 << 5) | (1 << 4)]
+    assert list(oracle.resident_topn(counts, 5)) == [(1 << 1) | (1 << 2) | (1 << 5) | (1 << 4) | (1 << 7)]
+    assert list(oracle.resident_topn(counts, 0)) == [0]
+    assert list(oracle.resident_topn(counts, 8)) == [0xFF]
+    # across words: 40 experts, the top 2 in the second word
+    c40 = [0] * 40
+    c40[33], c40[38] = 4, 4
+    assert list(oracle.resident_topn(c40, 2)) == [0, (1 << 1) | (1 << 6)]
+    # all equal: the lowest indices
+    assert list(oracle.resident_topn([3] * 40, 35)) == [0xFFFFFFFF, 0x7]
