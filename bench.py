@@ -249,7 +249,9 @@ def main():
         # routing of every chunk, read back once: resident picks (the only
         # routed pairs computed), misses and per-expert load
         res_bits = np.unpackbits(mask_np.view(np.uint8), bitorder="little")[:E].astype(bool)
-        hits, loads = [], []
+        hits, loads, online = [], [], []
+        acc = torch.zeros(E, dtype=torch.int64, device=dev)          # running popularity
+        learnt = torch.zeros_like(mask)                               # resident set learnt from earlier chunks
         for c in range(calls):
             ro = [{"topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
                    "counts": torch.empty(E, dtype=torch.int32, device=dev)}]
@@ -259,6 +261,12 @@ def main():
             cnt = ro[0]["counts"].cpu().numpy()
             hits.append(int(res_bits[idx].sum()))
             loads.append(float(cnt.max()) / (T * k / E))
+            if c > 0:
+                lbits = np.unpackbits(learnt.cpu().numpy().view(np.uint8), bitorder="little")[:E].astype(bool)
+                online.append(float(lbits[idx].mean()))
+            brx.counts_accumulate(acc, ro[0]["counts"], E, stream=stream)
+            brx.resident_topn(acc, E, int(res_bits.sum()), learnt, stream=stream)
+            torch.cuda.synchronize()
         # useful gate+up flops of the resident routed and the T shared token-expert pairs, per launch
         flops = 2.0 * (float(np.mean(hits)) + T) * d * (2 * f)
         if dom_us:
@@ -275,7 +283,10 @@ def main():
         dtype = "bf16-mfma/fp32"
         zipf_stats = {"hit_rate": round(sum(hits) / (calls * T * k), 4),
                       "misses_per_chunk": round(T * k - float(np.mean(hits)), 1),
-                      "max_over_mean_load": round(float(np.max(loads)), 2)}
+                      "max_over_mean_load": round(float(np.max(loads)), 2),
+                      "online_resident_hit_rate": round(float(np.mean(online)), 4) if online else None,
+                      "static_hit_rate_same_chunks": round(sum(hits[1:]) / ((calls - 1) * T * k), 4)
+                      if calls > 1 else None}
     else:
         # useful gate+up flops of the T*k routed and T shared token-expert pairs
         flops = 2.0 * (T * k + T) * d * (2 * f)
