@@ -37,7 +37,7 @@ def build(force: bool = False) -> str:
     src = os.path.join(_HERE, "oracle.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+        subprocess.check_call(["gcc", "-O3", "-mavx2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
                                "-fno-fast-math", "-o", tmp, src, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

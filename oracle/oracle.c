@@ -134,14 +134,21 @@ void oracle_pack_codes(int bits, const uint8_t *codes, int64_t out, int64_t in, 
 
 static double code_offset(int bits) { return bits == 3 ? 3.5 : 1.5; }
 
-/* Dequantised matrix [out][in] in double: scale(block) * (code - c0). */
-void oracle_dequant(int bits, const uint8_t *mat, const uint16_t *scales, int64_t out, int64_t in, double *w) {
+/* Dequantised matrix [out][in] in double: scale(block) * (code - c0).
+ * Every element is computed on its own, so rows may be split over threads. */
+static void dequant_rows(int bits, const uint8_t *mat, const uint16_t *scales, int64_t out, int64_t in, double *w,
+                         int threads) {
     double c0 = code_offset(bits);
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
     for (int64_t r = 0; r < out; ++r)
         for (int64_t c = 0; c < in; ++c) {
             int64_t n = r * in + c;
             w[n] = oracle_half_to_double(scales[n / 256]) * ((double)oracle_code_at(bits, mat, out, in, r, c) - c0);
         }
+}
+
+void oracle_dequant(int bits, const uint8_t *mat, const uint16_t *scales, int64_t out, int64_t in, double *w) {
+    dequant_rows(bits, mat, scales, out, in, w, 1);
 }
 
 /* ---------------------------------------------------------------- router */
@@ -289,7 +296,12 @@ void oracle_expert_ffn(int bits, const uint8_t *codes, const uint16_t *scales, i
 }
 
 /* Same FFN for several inputs with the expert dequantised once up front
- * (the "grouped" evaluation); identical arithmetic per input vector. */
+ * (the "grouped" evaluation).  Inputs are taken TB at a time so that TB
+ * independent sums advance together, but every sum is still formed in the
+ * order oracle_expert_ffn uses (i ascending for g and v, j ascending for y;
+ * one rounded product, then one rounded add, per term), so each input's
+ * result is bit-for-bit the one oracle_expert_ffn computes. */
+#define TB 32
 void oracle_expert_ffn_grouped(int bits, const uint8_t *codes, const uint16_t *scales, int d, int f, int n_in,
                                const double *u /*[n_in][d]*/, double *y /*[n_in][d]*/, int threads) {
     int64_t mat_bytes = (int64_t)d * f * bits / 8;
@@ -297,34 +309,71 @@ void oracle_expert_ffn_grouped(int bits, const uint8_t *codes, const uint16_t *s
     double *Wg = (double *)malloc(sizeof(double) * (size_t)d * f);
     double *Wu = (double *)malloc(sizeof(double) * (size_t)d * f);
     double *Wd = (double *)malloc(sizeof(double) * (size_t)d * f);
-    oracle_dequant(bits, codes, scales, f, d, Wg);
-    oracle_dequant(bits, codes + mat_bytes, scales + mat_blocks, f, d, Wu);
-    oracle_dequant(bits, codes + 2 * mat_bytes, scales + 2 * mat_blocks, d, f, Wd);
+    dequant_rows(bits, codes, scales, f, d, Wg, threads);
+    dequant_rows(bits, codes + mat_bytes, scales + mat_blocks, f, d, Wu, threads);
+    dequant_rows(bits, codes + 2 * mat_bytes, scales + 2 * mat_blocks, d, f, Wd, threads);
+    int nblk = (n_in + TB - 1) / TB;
 #pragma omp parallel for schedule(dynamic) num_threads(threads > 0 ? threads : 1)
-    for (int t = 0; t < n_in; ++t) {
-        const double *ut = u + (int64_t)t * d;
-        double *h = (double *)malloc(sizeof(double) * (size_t)f);
+    for (int b = 0; b < nblk; ++b) {
+        int t0 = b * TB, nt = n_in - t0 < TB ? n_in - t0 : TB;
+        double *ub = (double *)calloc((size_t)d * TB, sizeof(double));   /* [i][t]: input i of token t0+t */
+        double *h = (double *)calloc((size_t)f * TB, sizeof(double));    /* [j][t] */
+        for (int t = 0; t < nt; ++t)
+            for (int i = 0; i < d; ++i) ub[(int64_t)i * TB + t] = u[(int64_t)(t0 + t) * d + i];
         for (int j = 0; j < f; ++j) {
-            double g = 0.0, v = 0.0;
+            double g[TB], v[TB];
+            for (int t = 0; t < TB; ++t) g[t] = v[t] = 0.0;
             for (int i = 0; i < d; ++i) {
-                g += Wg[(int64_t)j * d + i] * ut[i];
-                v += Wu[(int64_t)j * d + i] * ut[i];
+                double wg = Wg[(int64_t)j * d + i], wu = Wu[(int64_t)j * d + i];
+                for (int t = 0; t < TB; ++t) {
+                    g[t] += wg * ub[(int64_t)i * TB + t];
+                    v[t] += wu * ub[(int64_t)i * TB + t];
+                }
             }
-            h[j] = silu(g) * v;
+            for (int t = 0; t < TB; ++t) h[(int64_t)j * TB + t] = silu(g[t]) * v[t];
         }
         for (int i = 0; i < d; ++i) {
-            double s = 0.0;
-            for (int j = 0; j < f; ++j) s += Wd[(int64_t)i * f + j] * h[j];
-            y[(int64_t)t * d + i] = s;
+            double s[TB];
+            for (int t = 0; t < TB; ++t) s[t] = 0.0;
+            for (int j = 0; j < f; ++j) {
+                double wd = Wd[(int64_t)i * f + j];
+                for (int t = 0; t < TB; ++t) s[t] += wd * h[(int64_t)j * TB + t];
+            }
+            for (int t = 0; t < nt; ++t) y[(int64_t)(t0 + t) * d + i] = s[t];
         }
+        free(ub);
         free(h);
     }
     free(Wg);
     free(Wu);
     free(Wd);
 }
+#undef TB
 
 /* ----------------------------------------------------------------- layer */
+/* Grouped evaluation of expert e (e == E: the shared expert, all T tokens)
+ * for its n_in (token, pick) pairs, written to ys[(t*(k+1) + r)*d ...]. */
+#define GROUP_BIG 256
+static void group_expert(int bits, int e, int E, int k, int d, int f, int n_in, const int32_t *perm,
+                         const int32_t *offsets, const uint8_t *codes, const uint16_t *scales, const double *ud,
+                         double *ys, int threads) {
+    double *ug = (double *)malloc(sizeof(double) * (size_t)n_in * d);
+    double *yg = (double *)malloc(sizeof(double) * (size_t)n_in * d);
+    for (int i = 0; i < n_in; ++i) {
+        int t = (e == E) ? i : perm[offsets[e] + i] / k;
+        memcpy(ug + (int64_t)i * d, ud + (int64_t)t * d, sizeof(double) * (size_t)d);
+    }
+    oracle_expert_ffn_grouped(bits, codes, scales, d, f, n_in, ug, yg, threads);
+    for (int i = 0; i < n_in; ++i) {
+        int t, r;
+        if (e == E) { t = i; r = k; }
+        else { t = perm[offsets[e] + i] / k; r = perm[offsets[e] + i] % k; }
+        memcpy(ys + ((int64_t)t * (k + 1) + r) * d, yg + (int64_t)i * d, sizeof(double) * (size_t)d);
+    }
+    free(ug);
+    free(yg);
+}
+
 /* Full layer for T tokens.  codes/scales hold E+1 experts (E = shared).
  * Writes routing (idx, gate), the permutation, the miss list, and
  * out[T][d] = fp32(y_shared + sum over resident r, ascending, of gate_r * y_r).
@@ -358,25 +407,21 @@ int oracle_moe_layer(int bits, int E, int k, int d, int f, int T, const float *u
                               ys + p * d);
         }
     } else {
+        /* experts with many inputs one after another, each on every thread;
+         * then the others side by side, one thread each (each expert writes
+         * only its own (t, r) rows of ys, so the order does not matter) */
         for (int e = 0; e <= E; ++e) {
             int n_in = (e == E) ? T : counts[e];
-            if (n_in == 0 || (e < E && !resident(mask, e))) continue;
-            double *ug = (double *)malloc(sizeof(double) * (size_t)n_in * d);
-            double *yg = (double *)malloc(sizeof(double) * (size_t)n_in * d);
-            for (int i = 0; i < n_in; ++i) {
-                int t = (e == E) ? i : perm[offsets[e] + i] / k;
-                memcpy(ug + (int64_t)i * d, ud + (int64_t)t * d, sizeof(double) * (size_t)d);
-            }
-            oracle_expert_ffn_grouped(bits, codes + e * exp_bytes, scales + e * exp_blocks, d, f, n_in, ug, yg,
-                                      threads);
-            for (int i = 0; i < n_in; ++i) {
-                int t, r;
-                if (e == E) { t = i; r = k; }
-                else { t = perm[offsets[e] + i] / k; r = perm[offsets[e] + i] % k; }
-                memcpy(ys + ((int64_t)t * (k + 1) + r) * d, yg + (int64_t)i * d, sizeof(double) * (size_t)d);
-            }
-            free(ug);
-            free(yg);
+            if (n_in >= GROUP_BIG && (e == E || resident(mask, e)))
+                group_expert(bits, e, E, k, d, f, n_in, perm, offsets, codes + e * exp_bytes,
+                             scales + e * exp_blocks, ud, ys, threads);
+        }
+#pragma omp parallel for schedule(dynamic) num_threads(threads > 0 ? threads : 1)
+        for (int e = 0; e <= E; ++e) {
+            int n_in = (e == E) ? T : counts[e];
+            if (n_in > 0 && n_in < GROUP_BIG && (e == E || resident(mask, e)))
+                group_expert(bits, e, E, k, d, f, n_in, perm, offsets, codes + e * exp_bytes,
+                             scales + e * exp_blocks, ud, ys, 1);
         }
     }
     for (int t = 0; t < T; ++t)

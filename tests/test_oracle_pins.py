@@ -210,6 +210,79 @@ def test_gates_closed_form_and_sum():
         assert np.all(np.diff(sel) <= 0)
 
 
+# ------------------------------------------------------------------ margins
+# The margin of a token is the smallest gap between neighbours in the list
+# of its k+1 largest logits, sorted in descending order (all E logits when
+# E <= k+1): a margin above the rounding error of any summation order makes
+# the ordered top-k and the (k+1)-th exclusion unique.
+@pytest.mark.parametrize("z,k,expect", [
+    # smallest gap between ranks 1 and 2 (logits stored out of order)
+    ([2.0, 5.0, 0.0, 3.5, 4.0, 1.0], 3, 0.5),
+    # smallest gap between ranks k and k+1
+    ([5.0, 3.0, -1.0, 1.0, 0.875], 3, 0.125),
+    # a tiny gap below rank k+1 does not count
+    ([0.0, 5.0, 3.0, 1.0, -0.0009765625], 2, 2.0),
+    # an exact tie inside the top-(k+1) gives 0, wherever the tied pair sits
+    ([1.0, 2.0, 2.0, 0.0], 2, 0.0),
+    ([4.0, 1.0, 3.0, 1.0, -2.0], 3, 0.0),
+    # a tie exactly at ranks k+1 and k+2 does not count
+    ([5.0, 1.0, 3.0, 1.0, -2.0], 2, 2.0),
+    # E = k + 1: every logit is in the list
+    ([0.0, 1.0, 3.0], 2, 1.0),
+    # E = k: the k logits alone
+    ([1.0, 2.5], 2, 1.5),
+    # negative logits and a single gap
+    ([-7.0, -3.0], 1, 4.0),
+])
+def test_topk_margin_hand_examples(z, k, expect):
+    m = oracle.topk_margin(np.array([z], np.float32), k)
+    assert m.shape == (1,) and float(m[0]) == expect
+
+
+def test_topk_margin_against_numpy_sort():
+    """Brute force: np.sort of each row, gaps of its k+1 largest."""
+    rng = np.random.default_rng(21)
+    for E, k in ((16, 2), (16, 5), (64, 10), (512, 10), (11, 10)):
+        z = rng.standard_normal((300, E)).astype(np.float32)
+        z[:30, 3] = z[:30, 7]                      # planted ties, inside or outside the top
+        z[30:60] = np.round(z[30:60] * 8) / 8      # coarse grid: many equal gaps and ties
+        s = -np.sort(-z.astype(np.float64), axis=1)[:, : min(k + 1, E)]
+        ref = np.min(s[:, :-1] - s[:, 1:], axis=1)
+        got = oracle.topk_margin(z, k).astype(np.float64)
+        assert np.array_equal(got, ref.astype(np.float32).astype(np.float64)), (E, k)
+
+
+def test_topk_margin_sees_router_bias():
+    """The margin is taken on the biased logits that the top-k uses: a bias
+    that brings two experts within 2^-12 of each other must show up, and one
+    that separates them must too.  One-hot router rows and integer inputs
+    keep every logit exact."""
+    E, d, k = 8, 16, 3
+    Wr = np.zeros((E, d), np.float32)
+    for e in range(E):
+        Wr[e, e] = 1.0
+    u = np.zeros((1, d), np.float32)
+    u[0, :E] = [9, 1, 7, 3, 5, 0, 2, 4]            # unbiased top-4: 9, 7, 5, 4 -> margin 1
+    assert float(oracle.topk_margin(oracle.logits(u, Wr), k)[0]) == 1.0
+    bias = np.zeros(E, np.float32)
+    bias[4] = 2.0 - 2.0 ** -12                     # expert 4: 7 - 2^-12, next to expert 2's 7
+    assert float(oracle.topk_margin(oracle.logits(u, Wr, bias), k)[0]) == 2.0 ** -12
+    bias[:] = 0.0
+    bias[[0, 2, 4, 7]] = [30.0, 20.0, 10.0, 0.0]   # 39, 27, 15, 4 -> margin 11
+    assert float(oracle.topk_margin(oracle.logits(u, Wr, bias), k)[0]) == 11.0
+
+
+def test_generated_tokens_meet_the_margin():
+    """The token generator's guarantee, checked on its output with numpy."""
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 0)
+    x, attempts = W.draw_tokens(w, L["Wr"], None, range(64), rep=5)
+    z = synth.bf16_to_f32(x).astype(np.float64) @ L["Wr"].astype(np.float64).T
+    s = -np.sort(-z, axis=1)[:, : w.top_k + 1]
+    assert np.min(s[:, :-1] - s[:, 1:]) >= W.MARGIN * (1 - 1e-4)
+    assert attempts.max() >= 1                     # some tokens needed a redraw
+
+
 # ------------------------------------------------------------- permutation
 def test_permute_is_stable_sort():
     rng = np.random.default_rng(6)
