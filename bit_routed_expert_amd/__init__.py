@@ -77,13 +77,17 @@ def load_library(path: str = LIB_PATH):
     lib.strata_moe_kernel_names.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(ctypes.c_char_p), i32]
     lib.strata_status_str.restype = ctypes.c_char_p
     lib.strata_status_str.argtypes = [ctypes.c_int]
+    lib.strata_probe_hbm_read.restype = ctypes.c_int
+    lib.strata_probe_hbm_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.strata_probe_mfma_bf16.restype = ctypes.c_int
+    lib.strata_probe_mfma_bf16.argtypes = [i32, vp, i32, ctypes.POINTER(ctypes.c_double), vp]
     _lib = lib
     return lib
 
 
 EXPORTED_SYMBOLS = ("strata_moe_workspace_bytes", "strata_moe_route", "strata_moe_forward",
                     "strata_moe_counts_accumulate", "strata_moe_resident_topn", "strata_moe_kernel_names",
-                    "strata_status_str")
+                    "strata_status_str", "strata_probe_hbm_read", "strata_probe_mfma_bf16")
 
 
 def _ptr(t) -> Optional[int]:
@@ -185,3 +189,15 @@ def resident_topn(counts_acc, n_experts: int, n_resident: int, mask_out, stream=
     """mask_out = the n_resident most-picked experts (count desc, index asc)."""
     _check(load_library().strata_moe_resident_topn(_ptr(counts_acc), n_experts, n_resident, _ptr(mask_out),
                                                    _stream(stream)))
+
+
+def probe_hbm_read(buf, nbytes: int, sink, blocks: int, stream=None):
+    """Stream-read probe: every byte of buf loaded once (see strata_probe.h)."""
+    _check(load_library().strata_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)))
+
+
+def probe_mfma_bf16(iters: int, sink, blocks: int, stream=None) -> float:
+    """bf16 matrix-core probe; returns the launch's floating-point operations."""
+    fl = ctypes.c_double()
+    _check(load_library().strata_probe_mfma_bf16(iters, _ptr(sink), blocks, ctypes.byref(fl), _stream(stream)))
+    return fl.value

@@ -10,7 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstrata_moe.so")
 SOURCES = ["api.hip", "popularity.hip", "route.hip", "gemv.hip", "gemv_gu3.hip", "gemv_gu2.hip", "gemv_dn3.hip", "gemv_dn2.hip",
-           "gemm.hip", "gemm_gu3.hip", "gemm_gu2.hip", "gemm_dn3.hip", "gemm_dn2.hip", "combine.hip"]
+           "gemm.hip", "gemm_gu3.hip", "gemm_gu2.hip", "gemm_dn3.hip", "gemm_dn2.hip", "combine.hip",
+           "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for every kernel in this library.

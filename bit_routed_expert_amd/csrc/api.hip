@@ -16,6 +16,12 @@ thread_local hipError_t g_last_hip = hipSuccess;
 
 namespace strata {
 thread_local LaunchEvents g_launch_events;
+
+strata_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return STRATA_OK;
+    g_last_hip = e;
+    return STRATA_EHIP;
+}
 }  // namespace strata
 
 namespace {
@@ -28,7 +34,7 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr int SMALL_T = 8;
 
 struct Layout {
-    size_t counter, z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf,
+    size_t z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf,
         xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
@@ -55,7 +61,6 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.max_items = max_items_for(s, T);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-    l.counter = take(ALIGN);
     l.z = take(sizeof(float) * T * E * (sp ? 1 : route_logit_splits((int)d)));
     l.idx = take(4 * T * k);
     l.gate = take(4 * T * k);
@@ -84,6 +89,16 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.miss_count = take(4);
     l.total = o;
     return l;
+}
+
+// The larger-T kernels address the bf16 layer input (hi and lo pieces) and
+// h with 32-bit buffer offsets, and slots and permutation entries are int32:
+// token counts whose arrays would not fit are refused before any launch.
+bool fits_32bit(const strata_moe_shape &s, int64_t T) {
+    if (small_path(s, T)) return true;
+    const int64_t slots = T * s.top_k + T;
+    return 2 * T * s.d_model * 2 <= (int64_t)INT32_MAX && slots * s.d_ff * 4 <= (int64_t)INT32_MAX &&
+           slots <= (int64_t)INT32_MAX;
 }
 
 strata_status check_shape(const strata_moe_shape *s) {
@@ -116,7 +131,6 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.inv_rms = (float *)(ws + l.inv_rms);
     a.items = (WorkItem *)(ws + l.items);
     a.n_items = (int32_t *)(ws + l.n_items);
-    a.counter = (uint32_t *)(ws + l.counter);
     a.xq = (uint32_t *)(ws + l.xq);
     a.xsum = (int32_t *)(ws + l.xsum);
     a.xscl = (float *)(ws + l.xscl);
@@ -159,10 +173,7 @@ struct Recorder {
         rec.before();                               \
         hipError_t e_ = (call);                     \
         rec.after();                                \
-        if (e_ != hipSuccess) {                     \
-            g_last_hip = e_;                        \
-            return STRATA_EHIP;                     \
-        }                                           \
+        if (e_ != hipSuccess) return hip_status(e_); \
     } while (0)
 
 // Route (and, unless route_only, prepare the input digit planes) of one
@@ -187,7 +198,7 @@ extern "C" {
 
 size_t strata_moe_workspace_bytes(const strata_moe_shape *shape, int32_t T, int32_t L) {
     (void)L;
-    if (check_shape(shape) != STRATA_OK || T < 0) return 0;
+    if (check_shape(shape) != STRATA_OK || T < 0 || !fits_32bit(*shape, T)) return 0;
     return layout(*shape, T > 0 ? T : 1).total;
 }
 
@@ -223,6 +234,7 @@ strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_l
     if (st != STRATA_OK) return st;
     if (T < 0 || !layer || (xdtype != STRATA_X_BF16 && xdtype != STRATA_X_F32)) return STRATA_EINVAL;
     if (T == 0) return STRATA_OK;
+    if (!fits_32bit(*shape, T)) return STRATA_EUNSUPPORTED;
     if (!x || !layer->router_w || !ws) return STRATA_EINVAL;
     if (!aligned16(x) || !aligned16(ws) || !aligned16(layer->router_w)) return STRATA_EINVAL;
     const Layout l = layout(*shape, T);
@@ -252,6 +264,7 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         (flags & ~(uint32_t)STRATA_NORM_FIRST) || n_events < 0 || (n_events > 0 && !events))
         return STRATA_EINVAL;
     if (T == 0) return STRATA_OK;
+    if (!fits_32bit(*shape, T)) return STRATA_EUNSUPPORTED;
     if (!x || !y_last || !ws) return STRATA_EINVAL;
     if (!aligned16(x) || !aligned16(y_last) || !aligned16(ws) || (resid_out && !aligned16(resid_out)))
         return STRATA_EINVAL;

@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "strata_moe.h"
+
 namespace strata {
 
 constexpr int WAVE = 64;
@@ -151,7 +153,6 @@ struct LayerArgs {
     int32_t *bmiss;      // [T/256 blocks] per-block miss counts, then first miss-list entries
     WorkItem *items;     // work list
     int32_t *n_items;    // [1]
-    uint32_t *counter;   // self-resetting arrival counter
     // optional user copies of routing
     int32_t *u_idx;
     float *u_gate;
@@ -196,6 +197,10 @@ extern thread_local LaunchEvents g_launch_events;
         g_launch_events.start = nullptr;                                                                  \
         hipExtLaunchKernelGGL(KER, GRID, BLOCK, LDS, STREAM, ev0_, g_launch_events.stop, 0, __VA_ARGS__); \
     } while (0)
+
+// Status of a HIP call for the C ABI: STRATA_OK, or STRATA_EHIP with the
+// error kept for strata_status_str (per thread).
+strata_status hip_status(hipError_t e);
 
 // Launchers (one file each); return hipGetLastError() of their launches.
 hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);

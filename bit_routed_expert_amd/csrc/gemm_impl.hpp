@@ -374,9 +374,9 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
     // stores go through buffer resources spanning the tile's ntok rows, so
     // rows past ntok fall outside them and are dropped by the hardware
     const uint32_t rowb = 2u * f, nf = f / 32;
-    const __amdgpu_buffer_rsrc_t rhi = buf_rsrc(uniform_ptr(a.ha + it.slot0 * f), ntok * rowb);
+    const __amdgpu_buffer_rsrc_t rhi = buf_rsrc(uniform_ptr(a.ha + (int64_t)it.slot0 * f), ntok * rowb);
     const __amdgpu_buffer_rsrc_t rlo = buf_rsrc(uniform_ptr(a.ha + (slots + it.slot0) * f), ntok * rowb);
-    const __amdgpu_buffer_rsrc_t rhs = buf_rsrc(uniform_ptr(a.hs + it.slot0 * nf), ntok * nf * 4);
+    const __amdgpu_buffer_rsrc_t rhs = buf_rsrc(uniform_ptr(a.hs + (int64_t)it.slot0 * nf), ntok * nf * 4);
     const uint32_t vo = 4u * h * rowb + 2u * pos, vs = 4u * (4u * h * nf + (j0 >> 5));
 #pragma unroll
     for (int mi = 0; mi < NMT; ++mi) {
@@ -466,7 +466,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it
     if (!active) return;
     // rows past ntok fall outside the resource and are dropped
     const uint32_t rowb = 4u * d;
-    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(uniform_ptr(a.Y + it.slot0 * d), ntok * rowb);
+    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(uniform_ptr(a.Y + (int64_t)it.slot0 * d), ntok * rowb);
     const uint32_t vo = 4u * h * rowb + 4u * r0;
 #pragma unroll
     for (int mi = 0; mi < NMT; ++mi) {

@@ -50,7 +50,7 @@ strata_status strata_moe_counts_accumulate(int64_t *counts_acc, const int32_t *c
     if (!counts_acc || !counts || n_experts < 1 || n_experts > 1024) return STRATA_EINVAL;
     STRATA_LAUNCH(counts_accumulate_kernel, dim3((n_experts + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                   counts_acc, counts, n_experts);
-    return hipGetLastError() == hipSuccess ? STRATA_OK : STRATA_EHIP;
+    return hip_status(hipGetLastError());
 }
 
 strata_status strata_moe_resident_topn(const int64_t *counts_acc, int32_t n_experts, int32_t n_resident,
@@ -59,7 +59,7 @@ strata_status strata_moe_resident_topn(const int64_t *counts_acc, int32_t n_expe
         return STRATA_EINVAL;
     STRATA_LAUNCH(resident_topn_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, counts_acc, n_experts,
                   n_resident, mask_out);
-    return hipGetLastError() == hipSuccess ? STRATA_OK : STRATA_EHIP;
+    return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

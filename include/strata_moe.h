@@ -55,8 +55,9 @@
  *   graph and replayed with new contents in the same buffers.  Validation happens on the host before any launch and
  *   nothing is enqueued when it fails.  Calls that overlap on one workspace
  *   race.
- *   The workspace must be zero-filled before its first use; every call
- *   leaves its internal counters at zero again.
+ *   The workspace needs no initialisation: a call writes every part of it
+ *   that it reads, so what a previous call (or anything else) left there
+ *   does not change its results.
  *   x, y_last, resid_out, the workspace, router weights and codes must be
  *   16-byte aligned (hipMalloc and torch allocations are); a misaligned one
  *   is rejected with STRATA_EINVAL.
@@ -116,17 +117,42 @@ typedef struct {
     int32_t *pos;
 } strata_route_out;
 
-/* Bytes of workspace a call with this shape, T tokens and L layers needs. */
+/* Bytes of workspace a call with this shape, T tokens and L layers needs
+ * (the same for every L: layers reuse it in turn).  0 for an invalid or
+ * unsupported shape or token count.  The workspace holds the per-call state
+ * of one layer: router logits, picks, gates, the permutation, the work list,
+ * the quantised layer input and the experts' intermediate outputs.
+ * Larger-T calls (above 8 tokens) are limited to token counts whose bf16
+ * layer input (2*T*d*2 bytes) and SwiGLU activations ((T*k + T)*f*4 bytes)
+ * stay below 2^31 bytes (63,550 tokens for d = 2048, f = 768, k = 10). */
 size_t strata_moe_workspace_bytes(const strata_moe_shape *shape, int32_t T, int32_t L);
 
-/* Routing only (the router, top-k, gates and permutation of one layer) for
- * T tokens x [dev] [T][d] (bf16 or fp32) used as given.
+/* Routing only, for one layer: the router logits, the ordered top-k with
+ * its gates and the permutation that groups picks by expert (per-layer
+ * routing of 10 of 512 experts: greenbean-ai, "Strata 如何讓 12GB 顯卡跑
+ * Qwen3.8-Flash-Next？", section 一; the GPU runs the router: same page,
+ * section 二).  x: [dev] [T][d], bf16 or fp32, used as given (no
+ * normalisation).  out: [host] struct of [dev] outputs, any may be NULL.
+ * ws: [dev] workspace of strata_moe_workspace_bytes(shape, T, 1) bytes.
+ * EINVAL: a null x, router or workspace, T < 0, a bad dtype or a misaligned
+ * pointer; EUNSUPPORTED: a shape or token count outside the limits above;
+ * EWORKSPACE: ws_bytes too small; EHIP: a launch failed.
  * T = 0 is a no-op returning STRATA_OK. */
 strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_layer *layer, const void *x,
                                strata_xdtype xdtype, int32_t T, const strata_route_out *out, void *ws,
                                size_t ws_bytes, void *stream);
 
-/* Forward of L stacked layers for T tokens.
+/* Forward of L stacked layers for T tokens: per layer the routing above,
+ * the SwiGLU FFN of every picked resident expert and of the shared expert
+ * over the packed blocks (the GPU computes the router, the shared expert and
+ * the experts it holds: greenbean-ai, section 二; wiselychen.com technique 2
+ * "專家快取與 CPU／GPU 分工"; ~3-bit and ~2-bit weights dequantised as they
+ * are used: wiselychen.com technique 1 "低位元量化"), the weighted combine,
+ * and the residual add that feeds the next layer (a verify step runs its
+ * tokens through every layer in one batch: wiselychen.com technique 4 "MTP
+ * 推測解碼").  Errors as for strata_moe_route, plus EINVAL for L < 1, a
+ * null layer array, codes or scales, unknown flags or a mask without miss
+ * buffers, and EUNSUPPORTED for a layer bits value other than 0, 2 or 3.
  *   layers     [host] array of L layer structs.
  *   x          [dev] [T][d] bf16 or fp32, the first layer's residual stream x_0.
  *   flags      STRATA_NORM_FIRST or 0.

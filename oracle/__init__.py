@@ -74,10 +74,17 @@ def _load():
 
 
 def _threads() -> int:
+    """Threads the oracle uses: every CPU this process may run on, or fewer
+    when OMP_NUM_THREADS says so (a machine shared between jobs sets it to
+    this job's share)."""
     try:
-        return max(1, min(16, len(os.sched_getaffinity(0))))
+        n = len(os.sched_getaffinity(0))
     except Exception:  # pragma: no cover
-        return 4
+        n = os.cpu_count() or 4
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -185,10 +192,11 @@ def expert_ffn_grouped(bits: int, codes, scales, d: int, f: int, u: np.ndarray) 
 
 
 # ------------------------------------------------------------------- layer
-def moe_layer(bits, E, k, d, f, u, Wr, codes, scales, bias=None, mask=None, miss_cap=None, grouped=True):
+def moe_layer(bits, E, k, d, f, u, Wr, codes, scales, bias=None, mask=None, miss_cap=None, grouped=True,
+              threads=None):
     """One layer.  codes: uint8 of (E+1) experts, expert-major; scales: uint16.
     Returns a dict with idx, gate, counts, offsets, perm, pos, out, miss_te,
-    miss_w, miss_count."""
+    miss_w, miss_count.  threads: OpenMP threads (default: _threads())."""
     u = _c(u, np.float32)
     T = u.shape[0]
     Wr = _c(Wr, np.float32)
@@ -206,7 +214,7 @@ def moe_layer(bits, E, k, d, f, u, Wr, codes, scales, bias=None, mask=None, miss
     n = _load().oracle_moe_layer(bits, E, k, d, f, T, _p(u), _p(Wr), _p(b), _p(codes), _p(scales), _p(m),
                                  _p(r["idx"]), _p(r["gate"]), _p(r["counts"]), _p(r["offsets"]), _p(r["perm"]),
                                  _p(r["pos"]), _p(r["out"]), _p(r["miss_te"]), _p(r["miss_w"]), cap,
-                                 1 if grouped else 0, _threads())
+                                 1 if grouped else 0, _threads() if threads is None else int(threads))
     r["miss_count"] = n
     r["miss_te"] = r["miss_te"][: min(n, cap)]
     r["miss_w"] = r["miss_w"][: min(n, cap)]

@@ -34,13 +34,14 @@ def shape_of(w) -> brx.Shape:
     return brx.shape(w.n_experts, w.top_k, w.d_model, w.d_ff, w.bits)
 
 
-def run_forward(w, layers, x_dev, xdtype, T, flags=0, miss_cap=None, want_route=True):
-    """Run strata_moe_forward; returns numpy results."""
+def run_forward(w, layers, x_dev, xdtype, T, flags=0, miss_cap=None, want_route=True, ws_fill=0):
+    """Run strata_moe_forward; returns numpy results.  ws_fill: byte value
+    the workspace holds before the call."""
     t = torch()
     sh = shape_of(w)
     L = len(layers)
     nb = brx.workspace_bytes(sh, T, L)
-    ws = t.zeros(nb, dtype=t.uint8, device="cuda")
+    ws = t.full((nb,), ws_fill, dtype=t.uint8, device="cuda")
     y = t.empty((T, w.d_model), dtype=t.float32, device="cuda")
     resid = t.empty((T, w.d_model), dtype=t.float32, device="cuda")
     k, E = w.top_k, w.n_experts

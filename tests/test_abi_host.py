@@ -15,9 +15,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "strata_moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(strata_\w+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(strata_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,6 +122,35 @@ def test_route_validation_errors():
     assert f(ctypes.byref(sh), ctypes.byref(ly), None, 0, 4, None, 0x6000, need, None) == brx.STRATA_EINVAL
     assert f(ctypes.byref(sh), ctypes.byref(ly), 0x4000, 0, 4, None, 0x6000, need - 8, None) == \
         brx.STRATA_EWORKSPACE
+
+
+def test_token_count_limit_of_the_larger_T_path():
+    """Token counts whose bf16 layer input or SwiGLU activations would pass
+    2^31 bytes (32-bit buffer offsets) are refused before any launch."""
+    lib = brx.load_library()
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    ok_T, bad_T = 63550, 63551                 # (T*10 + T) * 768 * 4 <= 2^31 - 1
+    assert brx.workspace_bytes(sh, ok_T) > 0
+    assert lib.strata_moe_workspace_bytes(ctypes.byref(sh), bad_T, 1) == 0
+    ly = (brx.Layer * 1)(_fake_layer())
+    st = lib.strata_moe_forward(ctypes.byref(sh), ly, 1, 0x4000, 0, bad_T, 0, 0x5000, None, None, None, None, 0,
+                                None, 0x6000, 1 << 40, None, 0, None)
+    assert st == brx.STRATA_EUNSUPPORTED
+    lyr = _fake_layer()
+    st = lib.strata_moe_route(ctypes.byref(sh), ctypes.byref(lyr), 0x4000, 0, bad_T, None, 0x6000, 1 << 40, None)
+    assert st == brx.STRATA_EUNSUPPORTED
+
+
+def test_probe_validation_errors():
+    lib = brx.load_library()
+    assert lib.strata_probe_hbm_read(None, 1024, 0x1000, 4, None) == brx.STRATA_EINVAL
+    assert lib.strata_probe_hbm_read(0x1008, 1024, 0x1000, 4, None) == brx.STRATA_EINVAL   # misaligned
+    assert lib.strata_probe_hbm_read(0x1000, 1000, 0x2000, 4, None) == brx.STRATA_EINVAL   # not whole 16 B
+    assert lib.strata_probe_hbm_read(0x1000, 1024, 0x2000, 0, None) == brx.STRATA_EINVAL
+    fl = ctypes.c_double()
+    assert lib.strata_probe_mfma_bf16(0, 0x1000, 4, ctypes.byref(fl), None) == brx.STRATA_EINVAL
+    assert lib.strata_probe_mfma_bf16(16, 0x1000, 0, ctypes.byref(fl), None) == brx.STRATA_EINVAL
+    assert lib.strata_probe_mfma_bf16(16, None, 4, ctypes.byref(fl), None) == brx.STRATA_EINVAL
 
 
 def test_status_strings():

@@ -293,3 +293,26 @@ def test_zero_router_picks_lowest_indices(T):
     got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
     G.assert_route_equal(got["route"][0], ref)
     G.assert_close(got["y"], ref["out"])
+
+
+@pytest.mark.parametrize("name,T,masked,L", [("tiny", 1, True, 1), ("tiny", 4, True, 2), ("tiny", 20, True, 2),
+                                             ("decode", 1, False, 2), ("decode", 5, False, 2),
+                                             ("decode", 37, False, 1)])
+def test_workspace_contents_do_not_matter(name, T, masked, L):
+    """A workspace full of 0xFF bytes (NaN as fp32, -1 as int32) gives the
+    same results, bit for bit, as a zeroed one: every call writes what it
+    reads (one-token, T <= 8 and matrix-core paths, with and without a
+    mask, one and two layers)."""
+    mask = np.array([0b0110_1011_1001_0111], np.uint32) if masked else None
+    w, L0, x, T = _layer_case(name, T=T, with_mask=mask)
+    print(f"case workspace fill {name} T={T} masked={masked} L={L}", flush=True)
+    layers = [G.layer_to_dev(L0) for _ in range(L)]
+    a = G.run_forward(w, layers, G.dev(x), 0, T, flags=0)
+    b = G.run_forward(w, layers, G.dev(x), 0, T, flags=0, ws_fill=0xFF)
+    for key in ("y", "resid") + (("miss_te", "miss_w", "miss_count") if masked else ()):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    for ra, rb in zip(a["route"], b["route"]):
+        for key in ra:
+            np.testing.assert_array_equal(ra[key], rb[key], err_msg=key)
+    if L == 1:
+        G.assert_close(a["y"], _oracle_layer(w, L0, synth.bf16_to_f32(x))["out"])

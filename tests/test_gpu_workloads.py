@@ -2,10 +2,10 @@
 4096-token 2-bit prefill chunk and the Zipf-skewed masked prefill, plus
 ragged token counts on the larger-batch path.
 
-Routing (ids, gates, counts, offsets, permutation, miss list) is compared
-for every token; layer outputs for every token where the oracle is cheap
-(the verify stack, ragged cases) and on a seeded sample of tokens otherwise
-(the oracle evaluates those tokens' experts one by one).
+Routing (ids, gates, counts, offsets, permutation, miss list) and the
+layer outputs are compared for every token: the 4096-token calls (the 2-bit
+chunk and all eight chunks of the 32K-token Zipf prompt) against the grouped
+oracle, which evaluates each needed expert once for all its tokens.
 """
 from __future__ import annotations
 
@@ -105,7 +105,10 @@ def test_verify_stack_48_layers_five_tokens():
         assert np.max(np.abs(gr["topk_w"] - gate_g)) <= G.GATE_TOL, f"layer {l} gates"
 
 
-def _prefill_case(name, call=0, sample=48):
+def _prefill_case(name, call=0):
+    """One 4096-token call against the grouped oracle on the whole output
+    tensor: routing of every token, the permutation, the miss list and all
+    T x d outputs."""
     w = synth.WORKLOADS[name]
     T = w.tokens_per_call
     t0 = time.time()
@@ -113,34 +116,30 @@ def _prefill_case(name, call=0, sample=48):
     tok = range(call * T, (call + 1) * T)
     x, _ = W.draw_tokens(w, L["Wr"], L["bias"], tok)
     u = synth.bf16_to_f32(x)
-    z = oracle.logits(u, L["Wr"], L["bias"])
-    idx, gate = oracle.select(z, w.top_k)
-    counts, offsets, perm, pos = oracle.permute(idx, w.n_experts)
-    te, mw, nm = oracle.misses(idx, gate, L["mask"], T * w.top_k)
-    rows = np.sort(np.random.default_rng(1234 + call).choice(T, sample, replace=False))
-    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u[rows], L["Wr"], L["codes"],
-                           L["scales"], bias=L["bias"], mask=L["mask"], grouped=False)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, L["Wr"], L["codes"], L["scales"],
+                           bias=L["bias"], mask=L["mask"], grouped=True)
     print(f"{name} call {call}: oracle {time.time() - t0:.1f}s", flush=True)
     got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
-    gr = got["route"][0]
-    G.assert_route_equal(gr, dict(idx=idx, gate=gate, counts=counts, offsets=offsets, perm=perm, pos=pos))
-    r = G.assert_close(got["y"][rows], ref["out"], what=f"{name} sampled rows")
-    np.testing.assert_array_equal(got["resid"][rows], (u[rows] + got["y"][rows]).astype(np.float32))
+    G.assert_route_equal(got["route"][0], ref)
+    r = G.assert_close(got["y"], ref["out"], what=f"{name} call {call} output")
+    np.testing.assert_array_equal(got["resid"], (u + got["y"]).astype(np.float32))
     if L["mask"] is not None:
+        nm = ref["miss_count"]
         assert int(got["miss_count"][0]) == nm
-        np.testing.assert_array_equal(got["miss_te"][0][:nm], te)
-        assert np.max(np.abs(got["miss_w"][0][:nm] - mw)) <= G.GATE_TOL
-        hit = 1 - nm / (T * w.top_k)
-        print(f"hit rate {hit:.3f}, max expert load {counts.max()}, mean {counts.mean():.1f}")
-    print(f"{name} sampled max-abs/RMS {r:.2e}")
+        np.testing.assert_array_equal(got["miss_te"][0][:nm], ref["miss_te"])
+        assert np.max(np.abs(got["miss_w"][0][:nm] - ref["miss_w"])) <= G.GATE_TOL
+        print(f"hit rate {1 - nm / (T * w.top_k):.3f}, max expert load {ref['counts'].max()}, "
+              f"mean {ref['counts'].mean():.1f}")
+    print(f"{name} call {call} max-abs/RMS {r:.2e} over {T} x {w.d_model} outputs")
 
 
 def test_prefill_chunk_2bit_4096():
     _prefill_case("prefill_2bit")
 
 
-@pytest.mark.parametrize("call", [0, 7])
+@pytest.mark.parametrize("call", range(8))
 def test_zipf_prefill_masked_chunks(call):
+    """Each of the eight 4096-token chunks of the 32K-token prompt."""
     _prefill_case("zipf_prefill", call=call)
 
 
@@ -278,8 +277,25 @@ def test_mixed_bit_width_stack(name, T):
         ld.bits = b
         dl.append(ld)
     got = G.run_forward(base, dl, G.dev(x0), 0, T)
+    # each layer's own GPU input, from chained one-layer calls (the stacked
+    # call must equal the chain bit for bit)
+    t = _torch()
+    xc, xd, gpu_inputs = G.dev(x0), 0, [synth.bf16_to_f32(x0)]
+    for l in range(len(dl)):
+        one = G.run_forward(wb[widths[l]], [dl[l]], xc, xd, T, flags=(1 if l > 0 else 0))
+        xc, xd = t.from_numpy(one["resid"]).cuda(), 1
+        gpu_inputs.append(one["resid"])
+    np.testing.assert_array_equal(one["y"], got["y"])
+    np.testing.assert_array_equal(one["resid"], got["resid"])
     for l, r in enumerate(refs):
-        np.testing.assert_array_equal(got["route"][l]["topk_idx"], r["idx"], err_msg=f"layer {l} ids")
+        gr = got["route"][l]
+        np.testing.assert_array_equal(gr["topk_idx"], r["idx"], err_msg=f"layer {l} ids")
+        for key in ("counts", "offsets", "perm", "pos"):
+            np.testing.assert_array_equal(gr[key], r[key], err_msg=f"layer {l} {key}")
+        u_gpu = oracle.layer_input(gpu_inputs[l], l)
+        idx_g, gate_g = oracle.select(oracle.logits(u_gpu, Ls[l]["Wr"]), base.top_k)
+        np.testing.assert_array_equal(idx_g, r["idx"])
+        assert np.max(np.abs(gr["topk_w"] - gate_g)) <= G.GATE_TOL, f"layer {l} gates"
     G.assert_close(got["y"], refs[-1]["out"], what="last layer output")
     G.assert_close(got["resid"], xl, what="residual")
     assert isinstance(dl[1], brx.LayerData) and dl[1].bits == 2
