@@ -69,6 +69,10 @@ def load_library(path: str = LIB_PATH):
     lib.strata_moe_forward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), i32, vp, ctypes.c_int, i32,
                                        ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32, vp, vp, sz,
                                        ctypes.POINTER(ctypes.c_void_p), i32, vp]
+    lib.strata_moe_forward_noalloc.restype = ctypes.c_int
+    lib.strata_moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), i32, vp, ctypes.c_int,
+                                               i32, ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32,
+                                               vp, ctypes.POINTER(ctypes.c_void_p), i32, vp]
     lib.strata_moe_counts_accumulate.restype = ctypes.c_int
     lib.strata_moe_counts_accumulate.argtypes = [vp, vp, i32, vp]
     lib.strata_moe_resident_topn.restype = ctypes.c_int
@@ -87,7 +91,10 @@ def load_library(path: str = LIB_PATH):
 
 EXPORTED_SYMBOLS = ("strata_moe_workspace_bytes", "strata_moe_route", "strata_moe_forward",
                     "strata_moe_counts_accumulate", "strata_moe_resident_topn", "strata_moe_kernel_names",
-                    "strata_status_str", "strata_probe_hbm_read", "strata_probe_mfma_bf16")
+                    "strata_status_str", "strata_probe_hbm_read", "strata_probe_mfma_bf16",
+                    "strata_moe_forward_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # STRATA_NOALLOC_SCRATCH_BYTES
 
 
 def _ptr(t) -> Optional[int]:
@@ -178,6 +185,28 @@ def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_la
     _check(lib.strata_moe_forward(ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last),
                                   _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w), miss_cap, _ptr(miss_count),
                                   _ptr(ws), ws_bytes, ev, n_ev, _stream(stream)))
+
+
+def forward_noalloc(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, resid_out=None,
+                    route_outs: Optional[Sequence[dict]] = None, miss_te=None, miss_w=None, miss_cap: int = 0,
+                    miss_count=None, flags: int = 0, events: Optional[Sequence[int]] = None, stream=None):
+    """forward() on the library's fixed per-device scratch (no workspace; see
+    strata_moe_forward_noalloc)."""
+    lib = load_library()
+    L = len(layers)
+    c_layers = (Layer * L)(*[ly.as_c() for ly in layers])
+    c_ro = None
+    if route_outs is not None:
+        assert len(route_outs) == L
+        c_ro = (RouteOut * L)(*[_route_out(r) or RouteOut() for r in route_outs])
+    ev = None
+    n_ev = 0
+    if events:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        n_ev = len(events) // 2
+    _check(lib.strata_moe_forward_noalloc(ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last),
+                                          _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w), miss_cap,
+                                          _ptr(miss_count), ev, n_ev, _stream(stream)))
 
 
 def counts_accumulate(counts_acc, counts, n_experts: int, stream=None):

@@ -3,6 +3,8 @@
 // Nothing here allocates device memory or synchronises the stream.
 #include <string.h>
 
+#include <mutex>
+
 #include "strata_moe.h"
 #include "common.hpp"
 
@@ -328,6 +330,62 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         }
     }
     return STRATA_OK;
+}
+
+// ------------------------------------------------ no-allocation variant
+// The workspace of strata_moe_forward_noalloc: a fixed array in device
+// memory, one copy per device (created when the library's code is loaded on
+// that device, held until the process ends).  Host code must not use the
+// name `scratch` as an address: each device's copy is found once with
+// hipGetSymbolAddress and that address is what the kernels are given.
+static __device__ __align__(256) uint8_t scratch[STRATA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+// Address of the current device's scratch, looked up on its first use.
+strata_status device_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= MAX_DEVICES) return STRATA_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return STRATA_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return STRATA_OK;
+}
+
+}  // namespace
+
+strata_status strata_moe_forward_noalloc(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
+                                         const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags,
+                                         float *y_last, float *resid_out, const strata_route_out *route_out,
+                                         int32_t *miss_te, float *miss_w, int32_t miss_cap, int32_t *miss_count,
+                                         void *const *events, int32_t n_events, void *stream) {
+    strata_status st = check_shape(shape);
+    if (st != STRATA_OK) return st;
+    if (T < 0) return STRATA_EINVAL;
+    if (T > 0) {
+        if (!fits_32bit(*shape, T)) return STRATA_EUNSUPPORTED;
+        if (layout(*shape, T).total > STRATA_NOALLOC_SCRATCH_BYTES) return STRATA_EWORKSPACE;
+    }
+    void *ws = nullptr;
+    if (T > 0) {
+        st = device_scratch(&ws);
+        if (st != STRATA_OK) return st;
+    }
+    return strata_moe_forward(shape, layers, L, x, xdtype, T, flags, y_last, resid_out, route_out, miss_te, miss_w,
+                              miss_cap, miss_count, ws, T > 0 ? STRATA_NOALLOC_SCRATCH_BYTES : 0, events, n_events,
+                              stream);
 }
 
 }  // extern "C"

@@ -174,6 +174,27 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
                                  float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws, size_t ws_bytes,
                                  void *const *events, int32_t n_events, void *stream);
 
+/* strata_moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  The library keeps a fixed scratch
+ * array of STRATA_NOALLOC_SCRATCH_BYTES in device memory, one per device it
+ * runs on (its address found on the first call on that device), held until
+ * the process ends; this entry point allocates nothing and frees nothing.
+ * Every call on one GPU uses that GPU's array, so calls that overlap on one
+ * GPU race, whatever their streams; calls in sequence on a stream are fine.
+ * The array is never cleared: no part of it needs to start at zero (see the
+ * workspace note above).  Arguments, results and errors are those of
+ * strata_moe_forward, plus STRATA_EWORKSPACE when the call needs more than
+ * the array holds (strata_moe_workspace_bytes(shape, T, L) >
+ * STRATA_NOALLOC_SCRATCH_BYTES; for d = 2048, f = 768, top-10 that is
+ * T > 403), returned before anything is enqueued. */
+#define STRATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+strata_status strata_moe_forward_noalloc(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
+                                         const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags,
+                                         float *y_last, float *resid_out, const strata_route_out *route_out,
+                                         int32_t *miss_te, float *miss_w, int32_t miss_cap, int32_t *miss_count,
+                                         void *const *events, int32_t n_events, void *stream);
+
 /* Names of the kernels strata_moe_forward enqueues for one layer, in order,
  * for a token count T; returns how many (<= max) and writes static strings. */
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max);
