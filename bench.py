@@ -103,8 +103,15 @@ def parse():
     p.add_argument("--traffic-kernel", default=None,
                    help="kernel group the traffic summary is for (default: the workload's dominant kernel)")
     p.add_argument("--counters-from", metavar="CSV", help="write the matrix-core counter summary from a CSV")
+    p.add_argument("--stats-from", metavar="CSV",
+                   help="write profiles/kernel_stats_<workload>.md from a rocprofv3 --stats kernel_stats CSV")
+    p.add_argument("--stats-cmd", default="", help="the profiled command, recorded in the stats summary")
     a = p.parse_args()
     return a
+
+
+def _log(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def default_steps(workload):
@@ -360,6 +367,8 @@ def bench_workload(name, args, res, dev, probes, steps, warmup):
         dtype = "bf16-mfma/fp32"
         layer_flops = 2.0 * (float(np.mean(hits)) + T) * 3 * d * f * calls
         extra["layer_mfma_frac"] = round(layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        if not args.profile_only:
+            extra["coprocess"] = _coprocess_timing(res, sh, ws, ws_bytes, dev, step_layer=warmup % nrot)
         extra["routing"] = {"hit_rate": round(sum(hits) / (calls * T * k), 4),
                             "misses_per_chunk": round(T * k - float(np.mean(hits)), 1),
                             "max_over_mean_load": round(float(np.max(loads)), 2),
@@ -377,6 +386,7 @@ def bench_workload(name, args, res, dev, probes, steps, warmup):
 
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
+        _log(f"{name}: timed, CPU baseline next")
         cpu = _cpu_baseline(name, w, args.cpu_sample_s, bias=None if res.bias is None else res.bias.cpu().numpy(),
                             mask=res.mask_np)
     rec = {
@@ -398,6 +408,60 @@ def bench_workload(name, args, res, dev, probes, steps, warmup):
     return rec
 
 
+def _coprocess_timing(res, sh, ws, ws_bytes, dev, step_layer):
+    """The masked prompt with its misses computed on the host and merged
+    (strata_moe_forward_coprocess), chunk by chunk through one resident
+    layer, and the host's share alone (strata_moe_host_misses on the first
+    chunk's miss list)."""
+    import torch
+    import bit_routed_expert_amd as brx
+    import oracle
+    import synth
+    w = res.w
+    T, calls, k, d = res.T, res.calls, w.top_k, w.d_model
+    codes = np.empty(w.experts_total * w.code_bytes_per_expert, dtype=np.uint8)
+    synth.layer_codes_into(w, step_layer, codes.ctypes.data)
+    scales = synth.layer_scales(w, step_layer)
+    layer = res.layers[step_layer]
+    cap = T * k
+    hnb = brx.host_workspace_bytes(sh, T, cap)
+    hws = torch.empty(hnb, dtype=torch.uint8, pin_memory=True)
+    threads = oracle._threads()
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    resid = torch.empty((T, d), dtype=torch.float32, device=dev)
+    mte = torch.empty((cap, 2), dtype=torch.int32, device=dev)
+    mw = torch.empty(cap, dtype=torch.float32, device=dev)
+    mc = torch.zeros(1, dtype=torch.int32, device=dev)
+    aux = torch.cuda.Stream()
+    times = []
+    for rep in range(2):   # the first pass is untimed
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for c in range(calls):
+            brx.forward_coprocess(sh, [layer], [(codes, scales, w.bits)], res.xs[c % res.n_in], brx.X_BF16, T, y, ws,
+                                  ws_bytes, hws, hnb, threads, mte, mw, cap, mc, resid_out=resid, aux_stream=aux)
+        torch.cuda.synchronize()
+        times.append(time.time() - t0)
+    # the host's share alone: chunk 0's misses (its miss list from a plain masked forward)
+    brx.forward(sh, [layer], res.xs[0], brx.X_BF16, T, y, ws, ws_bytes, miss_te=mte, miss_w=mw, miss_cap=cap,
+                miss_count=mc)
+    torch.cuda.synchronize()
+    n = int(mc.cpu()[0])
+    te, gw = mte[:n].cpu().numpy(), mw[:n].cpu().numpy()
+    u = synth.bf16_to_f32(res.xs[0].cpu().numpy().view(np.uint16))
+    y_add = np.empty((T, d), np.float32)
+    hws_np = np.empty(brx.host_workspace_bytes(sh, T, n), np.uint8)
+    t0 = time.time()
+    brx.host_misses(sh, codes, scales, w.bits, u, T, te, gw, n, y_add, hws_np, hws_np.nbytes, threads)
+    host_s = time.time() - t0
+    macs = n * 3 * d * w.d_ff
+    return {"ms_per_prompt": round(times[-1] * 1e3, 2), "tokens_per_s": round(T * calls / times[-1], 1),
+            "host_misses_ms_per_chunk": round(host_s * 1e3, 2), "misses_chunk0": n,
+            "host_gflops": round(2 * macs / host_s / 1e9, 1), "host_isa": brx.host_isa(), "host_threads": threads,
+            "what": "each chunk: GPU routing and resident experts, miss list and input copied to the host on a "
+                    "second stream, host FFNs of the misses from host-resident packed weights, merged on the GPU"}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -405,6 +469,9 @@ def main():
         return
     if args.counters_from:
         counters_summary(args)
+        return
+    if args.stats_from:
+        stats_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the MoE layer path here is single-GPU "
@@ -417,6 +484,7 @@ def main():
     probes = None
     if not args.no_probes and not args.profile_only:
         probes = probe_peaks(dev)
+        _log(f"probes {probes['hbm_read_gbs']} GB/s, {probes['mfma_bf16_tflops']} TFLOP/s")
     todo = [args.workload] if args.workload != "all" else ["decode"] + [wl for _, wl in SUB_RECORDS]
     recs = {}
     cache = {}
@@ -441,7 +509,9 @@ def main():
             n_in = (warmup + steps) if cfg["inputs"] is None else cfg["inputs"]
             res = Resident(synth_name, nrot, n_in, dev)
         cache[name] = res
+        _log(f"{name}: {len(res.layers)} resident layers ready ({time.time() - t0:.1f} s)")
         recs[name] = bench_workload(name, args, res, dev, probes, steps, warmup)
+        _log(f"{name}: {recs[name]['value']} tokens/s, {recs[name]['ms_per_step']} ms/step ({time.time() - t0:.1f} s)")
         if name == "prefill_2bit":
             cache.clear()
     setup_s = time.time() - t0
@@ -465,7 +535,7 @@ def main():
         "cpu_baseline": head["cpu_baseline"],
     }
     for key in ("setup_layer_passes", "kernels_us", "layer_hbm_frac", "layer_frac_of_probed_read",
-                "layer_mfma_frac", "routing"):
+                "layer_mfma_frac", "routing", "coprocess"):
         if key in head:
             line[key] = head[key]
     if args.workload == "all":
@@ -605,6 +675,29 @@ def traffic_summary(args):
                  f"gpurun_out/pmc_{wl}_write/run_counter_collection.csv\n```\n\n")
         fh.write("TRAFFIC " + json.dumps(rec) + "\n")
     print(json.dumps(rec))
+
+
+def stats_summary(args):
+    """Kernel durations of a profiled run (rocprofv3 --kernel-trace --stats)."""
+    wl = args.workload if args.workload != "all" else "decode"
+    rows = _counter_rows(args.stats_from)
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{wl}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel durations under rocprofv3 ({wl} workload)\n\n")
+        fh.write("Command (from the repository root, `$REPO` = its absolute path):\n\n```\n")
+        fh.write((args.stats_cmd or "(not recorded)") + "\n")
+        fh.write(f"python3 bench.py --workload {wl} --stats-from <that run's run_kernel_stats.csv>\n```\n\n")
+        fh.write("| kernel | calls | avg us | min us | max us | % |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"].replace("|", "\\|")
+            if len(name) > 90:
+                name = name[:87] + "..."
+            fh.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |\n")
+        srcs = sorted(set(sum((cfg["sources"] for cfg in WORKLOADS.values()), [])))
+        fh.write("\nKERNELSTATS " + json.dumps(dict(workload=wl, source_sha256=source_hash(srcs))) + "\n")
+    print(path)
 
 
 MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_BUSY_CYCLES", "SQ_WAVES",

@@ -39,6 +39,10 @@ class Layer(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("resident_mask", ctypes.c_void_p), ("bits", ctypes.c_int32)]
 
 
+class HostLayer(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("bits", ctypes.c_int32)]
+
+
 class RouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
@@ -73,6 +77,18 @@ def load_library(path: str = LIB_PATH):
     lib.strata_moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), i32, vp, ctypes.c_int,
                                                i32, ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32,
                                                vp, ctypes.POINTER(ctypes.c_void_p), i32, vp]
+    lib.strata_moe_host_workspace_bytes.restype = sz
+    lib.strata_moe_host_workspace_bytes.argtypes = [ctypes.POINTER(Shape), i32, i32]
+    lib.strata_moe_host_isa.restype = ctypes.c_char_p
+    lib.strata_moe_host_isa.argtypes = []
+    lib.strata_moe_host_misses.restype = ctypes.c_int
+    lib.strata_moe_host_misses.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(HostLayer), vp, i32, vp, vp, i32, vp,
+                                           vp, sz, i32]
+    lib.strata_moe_forward_coprocess.restype = ctypes.c_int
+    lib.strata_moe_forward_coprocess.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer),
+                                                 ctypes.POINTER(HostLayer), i32, vp, ctypes.c_int, i32,
+                                                 ctypes.c_uint32, vp, vp, ctypes.POINTER(RouteOut), vp, vp, i32, vp,
+                                                 vp, sz, vp, sz, i32, vp, vp]
     lib.strata_moe_counts_accumulate.restype = ctypes.c_int
     lib.strata_moe_counts_accumulate.argtypes = [vp, vp, i32, vp]
     lib.strata_moe_resident_topn.restype = ctypes.c_int
@@ -92,7 +108,8 @@ def load_library(path: str = LIB_PATH):
 EXPORTED_SYMBOLS = ("strata_moe_workspace_bytes", "strata_moe_route", "strata_moe_forward",
                     "strata_moe_counts_accumulate", "strata_moe_resident_topn", "strata_moe_kernel_names",
                     "strata_status_str", "strata_probe_hbm_read", "strata_probe_mfma_bf16",
-                    "strata_moe_forward_noalloc")
+                    "strata_moe_forward_noalloc", "strata_moe_host_workspace_bytes", "strata_moe_host_isa",
+                    "strata_moe_host_misses", "strata_moe_forward_coprocess")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # STRATA_NOALLOC_SCRATCH_BYTES
 
@@ -230,3 +247,59 @@ def probe_mfma_bf16(iters: int, sink, blocks: int, stream=None) -> float:
     fl = ctypes.c_double()
     _check(load_library().strata_probe_mfma_bf16(iters, _ptr(sink), blocks, ctypes.byref(fl), _stream(stream)))
     return fl.value
+
+
+def _host_ptr(a) -> Optional[int]:
+    """Address of a host buffer: a numpy array, a CPU torch tensor or an int."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "ctypes"):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+def host_isa() -> str:
+    """Instruction set of the host consumer of the miss list."""
+    return load_library().strata_moe_host_isa().decode()
+
+
+def host_workspace_bytes(sh: Shape, T: int, miss_cap: int) -> int:
+    n = load_library().strata_moe_host_workspace_bytes(ctypes.byref(sh), T, miss_cap)
+    if n == 0:
+        raise StrataError(STRATA_EUNSUPPORTED, "shape not handled by the host consumer")
+    return n
+
+
+def host_misses(sh: Shape, codes, scales, bits: int, u, T: int, miss_te, miss_w, n_miss: int, y_add, host_ws,
+                host_ws_bytes: int, n_threads: int):
+    """y_add = per-token sum of gate * FFN_e(u_t) over the misses, on the host
+    (see strata_moe_host_misses); every argument is host memory."""
+    hl = HostLayer(_host_ptr(codes), _host_ptr(scales), int(bits))
+    _check(load_library().strata_moe_host_misses(ctypes.byref(sh), ctypes.byref(hl), _host_ptr(u), T,
+                                                 _host_ptr(miss_te), _host_ptr(miss_w), n_miss, _host_ptr(y_add),
+                                                 _host_ptr(host_ws), host_ws_bytes, n_threads))
+
+
+def forward_coprocess(sh: Shape, layers: Sequence[LayerData], host_layers: Sequence[tuple], x, xdtype: int, T: int,
+                      y_last, ws, ws_bytes: int, host_ws, host_ws_bytes: int, n_threads: int, miss_te, miss_w,
+                      miss_cap: int, miss_count, resid_out=None, route_outs: Optional[Sequence[dict]] = None,
+                      flags: int = 0, aux_stream=None, stream=None):
+    """forward() with every masked layer's misses computed on the host and
+    added in (see strata_moe_forward_coprocess).  host_layers: per layer a
+    (codes, scales, bits) tuple of host buffers; host_ws: page-locked host
+    memory (e.g. a pinned torch tensor)."""
+    lib = load_library()
+    L = len(layers)
+    c_layers = (Layer * L)(*[ly.as_c() for ly in layers])
+    c_host = (HostLayer * L)(*[HostLayer(_host_ptr(c), _host_ptr(s_), int(b)) for c, s_, b in host_layers])
+    c_ro = None
+    if route_outs is not None:
+        assert len(route_outs) == L
+        c_ro = (RouteOut * L)(*[_route_out(r) or RouteOut() for r in route_outs])
+    aux = None if aux_stream is None else (aux_stream if isinstance(aux_stream, int) else aux_stream.cuda_stream)
+    _check(lib.strata_moe_forward_coprocess(ctypes.byref(sh), c_layers, c_host, L, _ptr(x), xdtype, T, flags,
+                                            _ptr(y_last), _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w),
+                                            miss_cap, _ptr(miss_count), _ptr(ws), ws_bytes, _host_ptr(host_ws),
+                                            host_ws_bytes, n_threads, aux, _stream(stream)))

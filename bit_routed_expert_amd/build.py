@@ -28,13 +28,45 @@ def _compile(src: str) -> str:
     return obj
 
 
+# The host consumer of the miss list: one object per instruction set (the
+# library picks one at run time), built by the host compiler.
+HOST_SOURCE = "host_experts.cpp"
+HOST_ISAS = {"hx512": ["-mavx512f", "-mavx512bw", "-mavx512dq", "-mavx512vl", "-mfma"],
+             "hx256": ["-mavx2", "-mfma"]}
+CXX = os.environ.get("CXX_HOST", "g++")
+
+
+def _compile_host(ns: str) -> str:
+    obj = os.path.join(BUILD, f"host_experts_{ns}.o")
+    cmd = [CXX, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-psabi", *HOST_ISAS[ns], f"-DHX_NS={ns}",
+           "-I", os.path.join(HERE, "..", "include"),
+           "-c", os.path.join(CSRC, HOST_SOURCE), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host compile failed for {ns}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def _compile_host_common() -> str:
+    obj = os.path.join(BUILD, "host.o")
+    cmd = [CXX, "-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-I", os.path.join(HERE, "..", "include"),
+           "-c", os.path.join(CSRC, "host.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host compile failed for host.cpp:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source (always) and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        futs = [ex.submit(_compile, src) for src in SOURCES]
+        futs += [ex.submit(_compile_host, ns) for ns in HOST_ISAS]
+        futs.append(ex.submit(_compile_host_common))
+        objs = [f.result() for f in futs]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -7,6 +7,7 @@
 
 #include "strata_moe.h"
 #include "common.hpp"
+#include "host_experts.hpp"
 
 using namespace strata;
 
@@ -18,6 +19,17 @@ thread_local hipError_t g_last_hip = hipSuccess;
 
 namespace strata {
 thread_local LaunchEvents g_launch_events;
+
+strata_status check_shape(const strata_moe_shape *s) {
+    if (!s) return STRATA_EINVAL;
+    if (s->n_shared != 1 || s->top_k < 1 || s->top_k > 32 || s->n_experts < s->top_k || s->n_experts > 1024)
+        return STRATA_EINVAL;
+    if (s->d_model <= 0 || s->d_ff <= 0 || s->d_model % 128 || s->d_ff % 128) return STRATA_EINVAL;
+    if (s->bits != 3 && s->bits != 2) return STRATA_EUNSUPPORTED;
+    if (!gemv_supported(s->d_model, s->d_ff, s->bits)) return STRATA_EUNSUPPORTED;
+    if (!gemm_supported(s->d_model, s->d_ff)) return STRATA_EUNSUPPORTED;
+    return STRATA_OK;
+}
 
 strata_status hip_status(hipError_t e) {
     if (e == hipSuccess) return STRATA_OK;
@@ -101,17 +113,6 @@ bool fits_32bit(const strata_moe_shape &s, int64_t T) {
     const int64_t slots = T * s.top_k + T;
     return 2 * T * s.d_model * 2 <= (int64_t)INT32_MAX && slots * s.d_ff * 4 <= (int64_t)INT32_MAX &&
            slots <= (int64_t)INT32_MAX;
-}
-
-strata_status check_shape(const strata_moe_shape *s) {
-    if (!s) return STRATA_EINVAL;
-    if (s->n_shared != 1 || s->top_k < 1 || s->top_k > 32 || s->n_experts < s->top_k || s->n_experts > 1024)
-        return STRATA_EINVAL;
-    if (s->d_model <= 0 || s->d_ff <= 0 || s->d_model % 128 || s->d_ff % 128) return STRATA_EINVAL;
-    if (s->bits != 3 && s->bits != 2) return STRATA_EUNSUPPORTED;
-    if (!gemv_supported(s->d_model, s->d_ff, s->bits)) return STRATA_EUNSUPPORTED;
-    if (!gemm_supported(s->d_model, s->d_ff)) return STRATA_EUNSUPPORTED;
-    return STRATA_OK;
 }
 
 void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char *ws, int T) {
@@ -255,11 +256,100 @@ strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_l
     return route_layer(a, *shape, T, rec);
 }
 
-strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
-                                 const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
-                                 float *resid_out, const strata_route_out *route_out, int32_t *miss_te,
-                                 float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws, size_t ws_bytes,
-                                 void *const *events, int32_t n_events, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host side of a co-processing forward: per masked layer, the miss list and
+// the layer input are copied to the host (on `aux`, after the kernel that
+// completes the miss list), the host computes the missed experts while the
+// GPU runs the resident ones, and the sum is added on the GPU.
+struct Coproc {
+    const strata_moe_host_layer *host_layers;
+    char *hws;
+    HostLayout hl;
+    int n_threads;
+    hipStream_t aux;
+    hipEvent_t ev_miss = nullptr, ev_copied = nullptr;
+    ~Coproc() {
+        if (ev_miss) (void)hipEventDestroy(ev_miss);
+        if (ev_copied) (void)hipEventDestroy(ev_copied);
+    }
+};
+
+strata_status coproc_copy_out(Coproc &cp, const LayerArgs &a, hipStream_t s) {
+    const size_t xb = (size_t)a.T * a.d * (a.x_is_bf16 ? 2 : 4);
+    hipError_t e = hipEventRecord(cp.ev_miss, s);
+    if (e == hipSuccess && cp.aux != s) e = hipStreamWaitEvent(cp.aux, cp.ev_miss, 0);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cp.hws + cp.hl.mcount, a.miss_count, 4, hipMemcpyDeviceToHost, cp.aux);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cp.hws + cp.hl.mte, a.miss_te, (size_t)a.miss_cap * 8, hipMemcpyDeviceToHost, cp.aux);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cp.hws + cp.hl.mw, a.miss_w, (size_t)a.miss_cap * 4, hipMemcpyDeviceToHost, cp.aux);
+    if (e == hipSuccess) e = hipMemcpyAsync(cp.hws + cp.hl.xstage, a.x, xb, hipMemcpyDeviceToHost, cp.aux);
+    if (e == hipSuccess) e = hipEventRecord(cp.ev_copied, cp.aux);
+    return hip_status(e);
+}
+
+// Wait for the copies, compute the layer's missed experts on the host, and
+// enqueue their sum into the layer's output and residual stream.
+strata_status coproc_finish(Coproc &cp, const LayerArgs &a, int bits, const strata_moe_host_layer &hl_,
+                            float *yadd_dev, hipStream_t s) {
+    hipError_t e = hipEventSynchronize(cp.ev_copied);
+    if (e != hipSuccess) return hip_status(e);
+    const int T = a.T, d = a.d;
+    const int n = *(const int32_t *)(cp.hws + cp.hl.mcount);
+    if (n < 0 || n > a.miss_cap) return STRATA_EINVAL;   // cannot happen with miss_cap >= T*k
+    // the layer input the GPU used: x (bf16 or fp32), RMS-normalised when the layer normalises
+    float *u = (float *)(cp.hws + cp.hl.u);
+    const char *xs = cp.hws + cp.hl.xstage;
+    for (int t = 0; t < T; ++t) {
+        float *ur = u + (size_t)t * d;
+        for (int i = 0; i < d; ++i) {
+            if (a.x_is_bf16) {
+                const uint32_t b = (uint32_t)((const uint16_t *)xs)[(size_t)t * d + i] << 16;
+                memcpy(&ur[i], &b, 4);
+            } else {
+                ur[i] = ((const float *)xs)[(size_t)t * d + i];
+            }
+        }
+        if (a.normalize) {
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) ss += (double)ur[i] * ur[i];
+            const float inv = (float)(1.0 / sqrt(ss / d + (double)RMS_EPS));
+            for (int i = 0; i < d; ++i) ur[i] *= inv;
+        }
+    }
+    HostMissArgs h{};
+    h.E = a.E;
+    h.d = d;
+    h.f = a.f;
+    h.bits = bits;
+    h.T = T;
+    h.n_miss = n;
+    h.n_threads = cp.n_threads;
+    h.codes = hl_.codes;
+    h.scales = hl_.scales;
+    h.u = u;
+    h.miss_te = (const int32_t *)(cp.hws + cp.hl.mte);
+    h.miss_w = (const float *)(cp.hws + cp.hl.mw);
+    h.h = (float *)(cp.hws + cp.hl.h);
+    h.gstart = (int32_t *)(cp.hws + cp.hl.gstart);
+    h.order = (int32_t *)(cp.hws + cp.hl.order);
+    h.experts = (int32_t *)(cp.hws + cp.hl.experts);
+    h.y_add = (float *)(cp.hws + cp.hl.yadd);
+    run_host_misses(h);
+    e = hipMemcpyAsync(yadd_dev, h.y_add, (size_t)T * d * 4, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_add_rows(a, yadd_dev, s));
+}
+
+strata_status forward_impl(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L, const void *x,
+                           strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last, float *resid_out,
+                           const strata_route_out *route_out, int32_t *miss_te, float *miss_w, int32_t miss_cap,
+                           int32_t *miss_count, void *ws, size_t ws_bytes, void *const *events, int32_t n_events,
+                           void *stream, Coproc *cp) {
     strata_status st = check_shape(shape);
     if (st != STRATA_OK) return st;
     if (T < 0 || L < 1 || !layers || (xdtype != STRATA_X_BF16 && xdtype != STRATA_X_F32) || miss_cap < 0 ||
@@ -312,24 +402,81 @@ strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe
         a.miss_count = miss_count ? miss_count + l : (int32_t *)(w + lay.miss_count);
         a.out = (l == L - 1) ? y_last : (float *)(w + lay.out);
         a.x_next = (l == L - 1) ? resid_out : (float *)(w + (l % 2 ? lay.xres1 : lay.xres0));
+        const bool co = cp && a.mask;   // this layer's misses go to the host
         st = route_layer(a, *shape, T, rec);
         if (st != STRATA_OK) return st;
         if (small_path(*shape, T)) {
+            // the gate/up kernel completes the routing and the miss list
             if (gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff)) {
                 RUN(launch_gemv_gateup_small(a, (int)lay.max_items, rec.s));
+                if (co && (st = coproc_copy_out(*cp, a, rec.s)) != STRATA_OK) return st;
                 RUN(launch_gemv_down_one(a, rec.s));
             } else {
                 RUN(launch_gemv_gateup_multi(a, (int)lay.max_items, rec.s));
+                if (co && (st = coproc_copy_out(*cp, a, rec.s)) != STRATA_OK) return st;
                 RUN(launch_gemv_down_multi(a, (int)lay.max_items, rec.s));
                 RUN(launch_combine(a, rec.s));
             }
         } else {
+            if (co && (st = coproc_copy_out(*cp, a, rec.s)) != STRATA_OK) return st;
             RUN(launch_gemm_gateup(a, (int)lay.max_items, rec.s));
             RUN(launch_gemm_down(a, (int)lay.max_items, rec.s));
             RUN(launch_combine(a, rec.s));
         }
+        // the host's sum is staged in the expert-output area: the combine has
+        // read it (earlier on the stream) and the next layer writes it later
+        if (co && (st = coproc_finish(*cp, a, a.bits, cp->host_layers[l], (float *)(w + lay.Y), rec.s)) != STRATA_OK)
+            return st;
     }
     return STRATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
+                                 const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
+                                 float *resid_out, const strata_route_out *route_out, int32_t *miss_te,
+                                 float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws, size_t ws_bytes,
+                                 void *const *events, int32_t n_events, void *stream) {
+    return forward_impl(shape, layers, L, x, xdtype, T, flags, y_last, resid_out, route_out, miss_te, miss_w,
+                        miss_cap, miss_count, ws, ws_bytes, events, n_events, stream, nullptr);
+}
+
+strata_status strata_moe_forward_coprocess(const strata_moe_shape *shape, const strata_moe_layer *layers,
+                                           const strata_moe_host_layer *host_layers, int32_t L, const void *x,
+                                           strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
+                                           float *resid_out, const strata_route_out *route_out, int32_t *miss_te,
+                                           float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws,
+                                           size_t ws_bytes, void *host_ws, size_t host_ws_bytes, int32_t n_threads,
+                                           void *aux_stream, void *stream) {
+    strata_status st = check_shape(shape);
+    if (st != STRATA_OK) return st;
+    if (T < 0 || L < 1 || !layers || !host_layers || n_threads < 1) return STRATA_EINVAL;
+    if (T == 0) return STRATA_OK;
+    if (!host_supported(*shape)) return STRATA_EUNSUPPORTED;
+    if ((int64_t)miss_cap < (int64_t)T * shape->top_k || !miss_te || !miss_w || !miss_count || !host_ws)
+        return STRATA_EINVAL;
+    for (int l = 0; l < L; ++l) {
+        if (!layers[l].resident_mask) continue;
+        if (!host_layers[l].codes || !host_layers[l].scales) return STRATA_EINVAL;
+        const int hb = host_layers[l].bits ? host_layers[l].bits : shape->bits;
+        const int db = layers[l].bits ? layers[l].bits : shape->bits;
+        if (hb != db) return STRATA_EINVAL;
+    }
+    Coproc cp;
+    cp.host_layers = host_layers;
+    cp.hws = (char *)host_ws;
+    cp.hl = host_layout(shape->n_experts, shape->d_model, shape->d_ff, T, miss_cap);
+    if (host_ws_bytes < cp.hl.total) return STRATA_EWORKSPACE;
+    cp.n_threads = n_threads;
+    cp.aux = aux_stream ? (hipStream_t)aux_stream : (hipStream_t)stream;
+    hipError_t e = hipEventCreateWithFlags(&cp.ev_miss, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&cp.ev_copied, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_status(e);
+    return forward_impl(shape, layers, L, x, xdtype, T, flags, y_last, resid_out, route_out, miss_te, miss_w,
+                        miss_cap, miss_count, ws, ws_bytes, nullptr, 0, stream, &cp);
 }
 
 // ------------------------------------------------ no-allocation variant

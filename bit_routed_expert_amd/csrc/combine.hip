@@ -70,6 +70,38 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     }
 }
 
+// out[i] += add[i], then x_next[i] = x[i] + out[i] (4 values per thread).
+template <int XBF16>
+__global__ __launch_bounds__(256) void add_rows_kernel(LayerArgs a, const float *add) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= (int64_t)a.T * a.d) return;
+    const float4 v = *(const float4 *)(add + i);
+    float4 o = *(const float4 *)(a.out + i);
+    o = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+    *(float4 *)(a.out + i) = o;
+    if (a.x_next) {
+        float4 xv;
+        if (XBF16) {
+            const uint2 q = *(const uint2 *)((const uint16_t *)a.x + i);
+            xv = make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
+                             __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
+        } else {
+            xv = *(const float4 *)((const float *)a.x + i);
+        }
+        *(float4 *)(a.x_next + i) = make_float4(xv.x + o.x, xv.y + o.y, xv.z + o.z, xv.w + o.w);
+    }
+}
+
+hipError_t launch_add_rows(const LayerArgs &a, const float *add, hipStream_t s) {
+    const int64_t n4 = (int64_t)a.T * a.d / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    if (a.x_is_bf16)
+        hipLaunchKernelGGL(add_rows_kernel<1>, grid, dim3(256), 0, s, a, add);
+    else
+        hipLaunchKernelGGL(add_rows_kernel<0>, grid, dim3(256), 0, s, a, add);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s) {
     const int blocks = a.T * ((a.d + CB_COLS - 1) / CB_COLS);
     if (a.x_is_bf16)

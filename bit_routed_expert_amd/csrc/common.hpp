@@ -216,6 +216,8 @@ hipError_t launch_gemv_down_multi(const LayerArgs &a, int max_items, hipStream_t
 hipError_t launch_gemv_down_one(const LayerArgs &a, hipStream_t s);
 bool gemv_one_token(int T, int E, int k, int d, int f);   // T = 1 kernels apply
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
+// out += add and x_next = x + out over the layer's T x d values (misses computed elsewhere)
+hipError_t launch_add_rows(const LayerArgs &a, const float *add, hipStream_t s);
 hipError_t launch_gemm_prep(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gemm_gateup(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemm_down(const LayerArgs &a, int max_items, hipStream_t s);

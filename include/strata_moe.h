@@ -195,6 +195,74 @@ strata_status strata_moe_forward_noalloc(const strata_moe_shape *shape, const st
                                          int32_t *miss_te, float *miss_w, int32_t miss_cap, int32_t *miss_count,
                                          void *const *events, int32_t n_events, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Host-CPU consumer of the miss list.  The pages' engine computes the
+ * experts its GPU holds on the GPU and the others on the CPU at the same
+ * time, then adds the two (wiselychen.com, technique 2 "專家快取與 CPU／GPU 分工";
+ * digiland.tw, "Strata 實測", item 2 "CPU 與 GPU 的協同運算（Co-processing）";
+ * tutuge.me "⚙️ 125B 是怎么塞进游戏 PC 的").  Here the host evaluates, for
+ * every listed miss (t, e, gate), gate * FFN_e(u_t) from packed weights in
+ * host memory (the format above), in fp32 on host threads with AVX-512 when
+ * the CPU has it, else AVX2 (strata_moe_host_isa() says which; neither:
+ * STRATA_EUNSUPPORTED).  Results do not depend on the thread count.
+ * Limits: d_model <= 8192, d_ff <= 4096.
+ */
+
+/* [host] struct of [host] pointers: one layer's weights as the host holds
+ * them (same bytes as strata_moe_layer.codes / .scales). */
+typedef struct {
+    const uint8_t *codes;    /* (E+1) experts */
+    const uint16_t *scales;  /* fp16 bit patterns */
+    int32_t bits;            /* 3 or 2, or 0 = the shape's bits */
+} strata_moe_host_layer;
+
+/* Bytes of host workspace for T tokens and up to miss_cap misses per layer
+ * (0 for an invalid shape or one the host consumer does not handle). */
+size_t strata_moe_host_workspace_bytes(const strata_moe_shape *shape, int32_t T, int32_t miss_cap);
+
+/* "avx512", "avx2" or "none": the instruction set the host consumer uses. */
+const char *strata_moe_host_isa(void);
+
+/* Host only, synchronous: y_add[t] = sum over the misses of token t of
+ * gate * FFN_e(u_t) (rows of tokens without misses are set to 0).
+ *   u        [host] [T][d] fp32: the layer input the experts consume.
+ *   miss_te  [host] [n_miss][2] (t, e) with 0 <= t < T, 0 <= e < E; miss_w [host] [n_miss] gates.
+ *   y_add    [host] [T][d] fp32, written.
+ *   host_ws  [host] strata_moe_host_workspace_bytes(shape, T, n_miss) bytes.
+ *   n_threads >= 1 host threads.
+ * EINVAL: null pointers, a miss outside the ranges, n_threads < 1;
+ * EWORKSPACE: host_ws too small; EUNSUPPORTED: see above. */
+strata_status strata_moe_host_misses(const strata_moe_shape *shape, const strata_moe_host_layer *layer,
+                                     const float *u, int32_t T, const int32_t *miss_te, const float *miss_w,
+                                     int32_t n_miss, float *y_add, void *host_ws, size_t host_ws_bytes,
+                                     int32_t n_threads);
+
+/* strata_moe_forward with the misses of every masked layer computed on the
+ * host and added in: per masked layer, once the kernel that completes the
+ * miss list has been enqueued, the miss list and the layer input are copied
+ * to host_ws on aux_stream (after an event on `stream`, so the copies
+ * overlap the GPU's expert kernels; aux_stream may be NULL: then `stream`),
+ * the calling thread waits for those copies, computes the misses as
+ * strata_moe_host_misses does, and enqueues on `stream` a copy of their sum
+ * to the workspace and a kernel that adds it to the layer's output
+ * (y = y_resident + y_misses, then x_next = x + y).  The next layer starts
+ * from that residual.  The call returns once the last layer's host work is
+ * done and its add is enqueued: host_ws must stay untouched until `stream`
+ * is synchronised.  host_layers: [host] array of L structs (used for masked
+ * layers).  host_ws: [host] strata_moe_host_workspace_bytes(shape, T,
+ * miss_cap) bytes, page-locked (hipHostMalloc) so that the copies run
+ * asynchronously.  miss_cap must be at least T*k (no miss is left out).
+ * Layers without a mask run as in strata_moe_forward.  Errors as for
+ * strata_moe_forward and strata_moe_host_misses; the HIP events it needs are
+ * created and destroyed inside the call. */
+strata_status strata_moe_forward_coprocess(const strata_moe_shape *shape, const strata_moe_layer *layers,
+                                           const strata_moe_host_layer *host_layers, int32_t L, const void *x,
+                                           strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
+                                           float *resid_out, const strata_route_out *route_out, int32_t *miss_te,
+                                           float *miss_w, int32_t miss_cap, int32_t *miss_count, void *ws,
+                                           size_t ws_bytes, void *host_ws, size_t host_ws_bytes, int32_t n_threads,
+                                           void *aux_stream, void *stream);
+
 /* Names of the kernels strata_moe_forward enqueues for one layer, in order,
  * for a token count T; returns how many (<= max) and writes static strings. */
 int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max);
