@@ -21,7 +21,7 @@ bool gemv_one_token(int T, int E, int k, int d, int f) {
     if (T != 1 || k + 1 > 12) return false;
     const int Rd = 64 / unit_slices(f, 8), Rg = 64 / unit_slices(d, 8);
     return 4 * (size_t)down_one_lds_words(k, f, Rd) <= LDS_LIMIT &&
-           4 * ((size_t)gateup_lds_words(d, Rg, 1, 1) + small_route_lds_words(E)) <= LDS_LIMIT;
+           4 * ((size_t)align4(gateup_lds_words(d, Rg, 1, 1)) + small_route_lds_words(E)) <= LDS_LIMIT;
 }
 
 // Compute units of the current device (cached per device).

@@ -277,6 +277,7 @@ struct GuLds {
         gu = scl + T * G;
     }
 };
+__host__ __device__ constexpr int align4(int words) { return (words + 3) & ~3; }
 __host__ __device__ inline int gateup_lds_words(int d, int R, int T, int nt) {
     const int S = 64 / R;
     const int dstride = (d / 32) * XPLANES * 4 + S * 4;
@@ -352,8 +353,11 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
 // wave) while the other waves stage the input digit planes, unit sums and
 // group scales, and runs its pick's rows; the last block writes the routing
 // outputs and the work list instead.
+// Registers are held to three waves per SIMD, so a grid of about 2,100
+// waves (ten picks plus the shared expert at f = 768) is resident at once.
 template <int BITS>
-__global__ __launch_bounds__(256) void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void gemv_gateup_small_kernel(LayerArgs a, int R, int route_off) {
     extern __shared__ uint32_t lds[];
     const GuLds g(lds, a.d, R, a.T, 1);
     const SmallRoute L(lds + route_off, a.E);
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_small_kernel(LayerArgs a, int
     const int b = blockIdx.x / wg_per_item;   // 0: shared expert, else pick b - 1
     if (b > 0 && threadIdx.x < 64) {
         WorkItem r{};
-        const bool ok = one_token_item(a, b - 1, r);
+        const bool ok = one_token_item(a, b - 1, L.cand, r);
         if (threadIdx.x == 0) {
             L.tmp[0] = ok ? r.expert : -1;
             L.tmp[1] = r.slot0;
@@ -790,7 +794,7 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
 template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int R = 64 / unit_slices(a.d, 8);
     const int G = a.f % (2 * R) == 0 ? 2 : 1;   // the result area holds up to four wave pairs' rows
-    const int off = gateup_lds_words(a.d, R, 1, 1);
+    const int off = align4(gateup_lds_words(a.d, R, 1, 1));   // the routing state is 16-byte aligned
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E));
     if (a.T != 1 || lds > LDS_LIMIT) return hipErrorInvalidValue;
     STRATA_LAUNCH(gemv_gateup_small_kernel<BITS>, dim3(max_items * (a.f / (G * R)) + 1), dim3(128 * G), lds, s, a,
@@ -802,7 +806,7 @@ template <int BITS> hipError_t gateup_small_launch(const LayerArgs &a, int max_i
 // code tiles, ~200 VGPRs), plus the routing writer.
 template <int BITS> hipError_t gateup_multi_launch(const LayerArgs &a, int max_items, int cus, hipStream_t s) {
     const int R = 64 / unit_slices(a.d, 8), upl = (a.d / 32) / (64 / R);
-    const int off = gateup_lds_words(a.d, R, a.T, ITEM_TOK);
+    const int off = align4(gateup_lds_words(a.d, R, a.T, ITEM_TOK));
     const size_t lds = 4 * ((size_t)off + small_route_lds_words(a.E) + 3 + small_route_table_words(a.T, a.k));
     const int jobs = max_items * (a.f / (R / 2)), wpb = 8;
     const int grid = std::min((jobs + wpb - 1) / wpb, std::max(1, cus)) + 1;

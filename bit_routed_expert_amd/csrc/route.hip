@@ -326,6 +326,7 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
 // the logits inv_rms[t] * z + bias and their top-k.
 __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
     __shared__ float zrow[4][1024];
+    __shared__ __attribute__((aligned(16))) uint32_t cand[4][TOPK_LDS_WORDS];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= a.T) return;
     const int E = a.E, ns = a.zsplit;
@@ -349,9 +350,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(LayerArgs a) {
         if (e < E) zr[e] = acc;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the row is read back by other lanes
-    wave_topk(zr, E, a.k, a.inv_rms[t], a.bias, a.idx + (size_t)t * a.k, a.gate + (size_t)t * a.k,
-              a.u_idx ? a.u_idx + (size_t)t * a.k : nullptr, a.u_gate ? a.u_gate + (size_t)t * a.k : nullptr,
-              nullptr, nullptr);
+    wave_topk(zr, E, a.k, a.inv_rms[t], a.bias, cand[threadIdx.x >> 6], a.idx + (size_t)t * a.k,
+              a.gate + (size_t)t * a.k, a.u_idx ? a.u_idx + (size_t)t * a.k : nullptr,
+              a.u_gate ? a.u_gate + (size_t)t * a.k : nullptr, nullptr, nullptr);
 }
 
 // ------------------------------------------------ permutation (larger T)

@@ -55,14 +55,70 @@ __device__ __forceinline__ float wave_allsum_f32(float v) {
 }
 #undef WAVE_BFLY
 
-// Ordered top-k of E logits z[e] * scale + bias[e] by one wave (JM = E/64
-// rounded up to 8 or 16); lane r < k ends with pick r: *e_out, *z_out.  Each
-// lane sorts its JM candidates by (value desc, index asc); a round takes the
-// wave maximum of the lanes' head values (32-bit), then the smallest head
-// index among the lanes holding it; the owning lane pops its head.
+// LDS scratch of one wave's top-k (16-byte aligned): TOPK_CAND candidate
+// entries of 64 bits, value key << 32 | ~expert index, so a larger entry is
+// an earlier pick.
+constexpr int TOPK_CAND = 64;
+constexpr int TOPK_LDS_WORDS = 2 * TOPK_CAND;
+
+// Selection by rounds (any number of equal keys; few registers): a round
+// takes each lane's best remaining key (value desc, index asc) by a scan,
+// the wave maximum of those values, then the smallest index among the lanes
+// holding it; the owning lane clears that key.  Lane r < k ends with pick r
+// in (*my_e, *my_k).  Keys are nonzero except for empty places.
+template <int JM>
+__device__ __forceinline__ void topk_rounds(uint32_t (&kv)[JM], int k, int *my_e, uint32_t *my_k) {
+    const int lane = threadIdx.x & 63;
+    for (int r = 0; r < k; ++r) {
+        uint32_t bk = 0u;
+        int bj = 0;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {   // a strict > keeps the lowest index among equal values
+            bj = kv[j] > bk ? j : bj;
+            bk = kv[j] > bk ? kv[j] : bk;
+        }
+        const uint32_t m = wave_allmax_u32(bk);
+        const uint32_t e = wave_allmin_u32(bk == m ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu);
+        if (lane == r) {
+            *my_e = (int)e;
+            *my_k = m;
+        }
+        if (bk == m && (uint32_t)(lane + 64 * bj) == e) {   // the owner clears its key
+#pragma unroll
+            for (int j = 0; j < JM; ++j)
+                if (j == bj) kv[j] = 0u;
+        }
+    }
+}
+
+// Inclusive prefix sum over the wave (row shifts, then the row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Ordered top-k (k <= 32) of E logits z[e] * scale + bias[e] by one wave
+// (JM = E/64 rounded up to 8 or 16), by (value desc, index asc); lane r < k
+// ends with pick r: *e_out, *z_out.  cand: this wave's TOPK_LDS_WORDS of LDS.
+//   1. P = the k-th largest of the 64 lane maxima, cut to its top 16 bits:
+//      at least k keys are >= P, so every pick is >= P.  Found two bits at a
+//      time from the top (a value is kept while k lanes reach it, counted
+//      with wave ballots).
+//   2. The keys >= P (usually a few more than k) are packed into LDS at a
+//      wave prefix sum of the per-lane counts; when no lane holds more than
+//      two (the usual case) they are its two largest keys, found as the keys
+//      are formed.
+//   3. Each candidate's rank is the number of larger entries (LDS reads that
+//      every lane shares); rank r < k is pick r.
+// More than TOPK_CAND candidates (many equal values) take the rounds above.
 template <int JM>
 __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
-                                                     int *e_out, float *z_out) {
+                                                     uint32_t *cand, int *e_out, float *z_out) {
     const int lane = threadIdx.x & 63;
     float zv[JM], bv[JM];
 #pragma unroll
@@ -73,51 +129,91 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
 #pragma unroll
         for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
     }
-    uint32_t kv[JM], ki[JM];   // value key (0 = empty), expert index
+    uint32_t kv[JM];   // value key (0 = empty)
+    // the lane's two largest keys in order (value desc, place asc) and their places
+    uint32_t mx = 0u, sx = 0u;
+    int jm = 0, js = 0;
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
         const int e = lane + 64 * j;
         kv[j] = (e < E) ? f32_key(zv[j] * scale + bv[j]) : 0u;
-        ki[j] = (uint32_t)e;
+        const bool top = kv[j] > mx, second = !top && kv[j] > sx;
+        js = top ? jm : (second ? j : js);
+        sx = top ? mx : (second ? kv[j] : sx);
+        jm = top ? j : jm;
+        mx = top ? kv[j] : mx;
     }
-    // bitonic sort, descending by (kv, -ki); indices of one lane increase with j
+    const uint32_t ku = (uint32_t)k;
+    uint32_t P = 0u;
 #pragma unroll
-    for (int kk = 2; kk <= JM; kk <<= 1)
+    for (int sh = 30; sh >= 16; sh -= 2) {
+        const uint32_t c1 = P | (1u << sh), c2 = P | (2u << sh), c3 = P | (3u << sh);
+        const bool b1 = __popcll(__ballot(mx >= c1)) >= ku;
+        const bool b2 = __popcll(__ballot(mx >= c2)) >= ku;
+        const bool b3 = __popcll(__ballot(mx >= c3)) >= ku;
+        P = b3 ? c3 : (b2 ? c2 : (b1 ? c1 : P));
+    }
+    int cnt = 0;
 #pragma unroll
-        for (int jj = kk >> 1; jj > 0; jj >>= 1)
+    for (int j = 0; j < JM; ++j) cnt += kv[j] >= P ? 1 : 0;
+    uint64_t *c64 = (uint64_t *)cand;
+    int C;
+    if (__ballot(cnt > 2) == 0) {   // the usual case: the candidates are the lanes' two largest keys
+        const int incl = wave_incl_scan(cnt);
+        C = __builtin_amdgcn_readlane(incl, 63);
+        const int pos = incl - cnt;
+        if (cnt >= 1 && pos < TOPK_CAND) c64[pos] = ((uint64_t)mx << 32) | (uint32_t)~(uint32_t)(lane + 64 * jm);
+        if (cnt == 2 && pos + 1 < TOPK_CAND)
+            c64[pos + 1] = ((uint64_t)sx << 32) | (uint32_t)~(uint32_t)(lane + 64 * js);
+    } else {
+        const int incl = wave_incl_scan(cnt);
+        C = __builtin_amdgcn_readlane(incl, 63);
+        int pos = incl - cnt;
 #pragma unroll
-            for (int i = 0; i < JM; ++i) {
-                const int l = i ^ jj;
-                if (l > i) {
-                    const bool desc = (i & kk) == 0;
-                    const bool a_first = kv[i] > kv[l] || (kv[i] == kv[l] && ki[i] < ki[l]);
-                    const bool sw = desc ? !a_first : a_first;
-                    const uint32_t tv = kv[i], ti = ki[i];
-                    kv[i] = sw ? kv[l] : tv;
-                    ki[i] = sw ? ki[l] : ti;
-                    kv[l] = sw ? tv : kv[l];
-                    ki[l] = sw ? ti : ki[l];
-                }
+        for (int j = 0; j < JM; ++j) {
+            if (kv[j] >= P) {
+                if (pos < TOPK_CAND) c64[pos] = ((uint64_t)kv[j] << 32) | (uint32_t)~(uint32_t)(lane + 64 * j);
+                ++pos;
             }
+        }
+    }
     int my_e = 0;
     uint32_t my_k = 0x80000000u;   // key of 0.0 for lanes past k
-    for (int r = 0; r < k; ++r) {
-        // largest head value, then the smallest expert index among the
-        // lanes holding it; both land in every lane
-        const uint32_t m = wave_allmax_u32(kv[0]);
-        const uint32_t e = wave_allmin_u32(kv[0] == m ? ki[0] : 0xFFFFFFFFu);
-        if (lane == r) {
-            my_e = (int)e;
-            my_k = m;
-        }
-        if (kv[0] == m && ki[0] == e) {  // the owner pops its head
+    if (C <= TOPK_CAND) {
+        // entries are read 16 (or four) at a time: zero ones rank below every key
+        const int Cp = C <= 16 ? 16 : (C + 3) & ~3;
+        if (lane >= C && lane < Cp) c64[lane] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t key = lane < C ? c64[lane] : 0u;
+        int rank = 0;
+        if (C <= 16) {
+            ulonglong2 q[8];
 #pragma unroll
-            for (int j = 0; j < JM - 1; ++j) {
-                kv[j] = kv[j + 1];
-                ki[j] = ki[j + 1];
+            for (int i = 0; i < 8; ++i) q[i] = *(const ulonglong2 *)(c64 + 2 * i);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rank += (q[i].x > key ? 1 : 0) + (q[i].y > key ? 1 : 0);
+        } else {
+            for (int i = 0; i < Cp; i += 4) {
+                const ulonglong2 a = *(const ulonglong2 *)(c64 + i), b = *(const ulonglong2 *)(c64 + i + 2);
+                rank += (a.x > key ? 1 : 0) + (a.y > key ? 1 : 0) + (b.x > key ? 1 : 0) + (b.y > key ? 1 : 0);
             }
-            kv[JM - 1] = 0u;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < C && rank < k) c64[rank] = key;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < k) {
+            const uint64_t v = c64[lane];
+            my_k = (uint32_t)(v >> 32);
+            my_e = (int)~(uint32_t)v;
+        }
+    } else {
+        topk_rounds<JM>(kv, k, &my_e, &my_k);
     }
     *e_out = my_e;
     *z_out = __uint_as_float((my_k & 0x80000000u) ? (my_k & 0x7FFFFFFFu) : ~my_k);
@@ -125,15 +221,15 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
 
 // Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
 __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float scale, const float *bias,
-                                          int32_t *idx_out, float *gate_out, int32_t *idx_out2, float *gate_out2,
-                                          int32_t *idx_lds, float *gate_lds) {
+                                          uint32_t *cand, int32_t *idx_out, float *gate_out, int32_t *idx_out2,
+                                          float *gate_out2, int32_t *idx_lds, float *gate_lds) {
     const int lane = threadIdx.x & 63;
     int e;
     float v;
     if (E <= 512)
-        wave_topk_picks_fast<8>(z, E, k, scale, bias, &e, &v);
+        wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v);
     else
-        wave_topk_picks_fast<16>(z, E, k, scale, bias, &e, &v);
+        wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v);
     const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float p = (lane < k) ? expf(v - top) : 0.f;
     const float s = wave_allsum_f32(p);
@@ -175,27 +271,34 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp /* >= 16 ints */,
 }
 
 // ----------------------------------------------------- small-T routing state
-// LDS words: per-expert token masks [E], resident-picked bitmap [32],
-// picks [256] (ids), gates [256], scratch [16].
-__host__ __device__ constexpr int small_route_lds_words(int E) { return E + 32 + 256 + 256 + 16; }
+// LDS words (base 16-byte aligned): top-k scratch of up to 8 waves
+// [8][TOPK_LDS_WORDS], per-expert token masks [E], resident-picked bitmap
+// [32], picks [256] (ids), gates [256], scratch [16].
+constexpr int SMALL_ROUTE_WAVES = 8;
+__host__ __device__ constexpr int small_route_lds_words(int E) {
+    return SMALL_ROUTE_WAVES * TOPK_LDS_WORDS + E + 32 + 256 + 256 + 16;
+}
 
 struct SmallRoute {
+    uint32_t *cand;
     int32_t *tokmask;
     uint32_t *picked;
     int32_t *sidx;
     float *sgate;
     int32_t *tmp;
     __device__ SmallRoute(uint32_t *base, int E)
-        : tokmask((int32_t *)base),
-          picked(base + E),
-          sidx((int32_t *)(base + E + 32)),
-          sgate((float *)(base + E + 32 + 256)),
-          tmp((int32_t *)(base + E + 32 + 512)) {}
+        : cand(base),
+          tokmask((int32_t *)(base + SMALL_ROUTE_WAVES * TOPK_LDS_WORDS)),
+          picked(base + SMALL_ROUTE_WAVES * TOPK_LDS_WORDS + E),
+          sidx((int32_t *)(base + SMALL_ROUTE_WAVES * TOPK_LDS_WORDS + E + 32)),
+          sgate((float *)(base + SMALL_ROUTE_WAVES * TOPK_LDS_WORDS + E + 32 + 256)),
+          tmp((int32_t *)(base + SMALL_ROUTE_WAVES * TOPK_LDS_WORDS + E + 32 + 512)) {}
 };
 
-// Top-k of T <= 8 tokens (one wave per token) from the unnormalised logits
-// z[t][E] and the tokens' inverse RMS inv[t] (both may sit in LDS), then
-// per-expert token masks and the bitmap of picked resident experts.
+// Top-k of T <= 8 tokens (one wave per token, blocks of at most
+// SMALL_ROUTE_WAVES waves) from the unnormalised logits z[t][E] and the
+// tokens' inverse RMS inv[t] (both may sit in LDS), then per-expert token
+// masks and the bitmap of picked resident experts.
 __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const SmallRoute &L, const float *z,
                                                     const float *inv) {
     const int th = threadIdx.x, wave = th >> 6, nw = blockDim.x >> 6;
@@ -203,8 +306,8 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
     for (int i = th; i < E; i += blockDim.x) L.tokmask[i] = 0;
     if (th < 32) L.picked[th] = 0;
     for (int t = wave; t < T; t += nw)
-        wave_topk(z + t * E, E, k, inv[t], a.bias, nullptr, nullptr, nullptr, nullptr, L.sidx + t * k,
-                  L.sgate + t * k);
+        wave_topk(z + t * E, E, k, inv[t], a.bias, L.cand + (wave % SMALL_ROUTE_WAVES) * TOPK_LDS_WORDS, nullptr,
+                  nullptr, nullptr, nullptr, L.sidx + t * k, L.sgate + t * k);
     __syncthreads();
     if (th < T * k) {
         const int e = L.sidx[th];
@@ -223,14 +326,15 @@ __host__ __device__ __forceinline__ int tok_of(uint32_t tpk, int j) { return (in
 // work item of pick r (in top-k order): its expert and, as first slot, the
 // number of picks of lower experts (the slot small_route_write gives it).
 // Returns false when that expert is not resident.  Results are wave-uniform.
-__device__ __forceinline__ bool one_token_item(const LayerArgs &a, int r, WorkItem &it) {
+// cand: this wave's TOPK_LDS_WORDS of LDS.
+__device__ __forceinline__ bool one_token_item(const LayerArgs &a, int r, uint32_t *cand, WorkItem &it) {
     const int lane = threadIdx.x & 63, k = a.k;
     int e;
     float v;
     if (a.E <= 512)
-        wave_topk_picks_fast<8>(a.z, a.E, k, a.inv_rms[0], a.bias, &e, &v);
+        wave_topk_picks_fast<8>(a.z, a.E, k, a.inv_rms[0], a.bias, cand, &e, &v);
     else
-        wave_topk_picks_fast<16>(a.z, a.E, k, a.inv_rms[0], a.bias, &e, &v);
+        wave_topk_picks_fast<16>(a.z, a.E, k, a.inv_rms[0], a.bias, cand, &e, &v);
     const int er = __builtin_amdgcn_readlane(e, r);
     if (!is_resident(a.mask, er)) return false;
     it = WorkItem{er, (int)__popcll(__ballot(lane < k && e < er)), 1};
