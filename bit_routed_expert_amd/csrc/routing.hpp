@@ -251,12 +251,7 @@ __device__ __forceinline__ bool is_resident(const uint32_t *mask, int e) {
 // Exclusive scan of one int per thread over the block; *total = block sum.
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp /* >= 16 ints */, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o, WAVE);
-        if (lane >= o) inc += t;
-    }
+    const int inc = wave_incl_scan(v);
     __syncthreads();
     if (lane == 63) tmp[wave] = inc;
     __syncthreads();
