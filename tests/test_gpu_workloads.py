@@ -221,14 +221,17 @@ def test_wide_topk_and_shared_picks(bits, T):
                                             (1024, 8, 256, 128, 2, 20), (1000, 6, 384, 384, 3, 1),
                                             (1000, 6, 384, 384, 2, 5), (1000, 6, 384, 384, 3, 20),
                                             (256, 10, 2048, 768, 3, 1), (256, 10, 2048, 768, 2, 5),
-                                            (256, 10, 2048, 768, 3, 20)])
+                                            (256, 10, 2048, 768, 3, 20), (512, 32, 256, 128, 3, 1),
+                                            (512, 32, 256, 128, 3, 5), (1024, 32, 256, 128, 2, 8)])
 def test_wide_expert_counts_and_odd_widths(E, k, d, f, bits, T):
     """More than 512 experts (16 logits per lane in the top-k, the largest
     supported expert count), an expert count that is not a multiple of 64,
     the expert-pruned 256-expert full-size layer,
     and d = f = 384 (rows of 1.5 scale blocks, 12 units per row: 128-column
     scale steps on the matrix-core path) on the decode kernels (T = 1, 5)
-    and the matrix-core path (T = 20)."""
+    and the matrix-core path (T = 20); and k = 32, the largest top-k (40-60
+    keys reach the top-k's threshold, near its 64-candidate limit, and most
+    lanes hold more than two of them)."""
     w = synth.Workload(f"wide_E{E}_d{d}_b{bits}", E, k, d, f, bits, T, seed=0x5EED0B00 + E + d + bits)
     L = W.layer_data(w, 0)
     x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=13)
