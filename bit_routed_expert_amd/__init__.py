@@ -182,12 +182,10 @@ def route(sh: Shape, layer: LayerData, x, xdtype: int, T: int, out: dict, ws, ws
                                 ctypes.byref(ro) if ro is not None else None, _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, ws, ws_bytes: int,
-            resid_out=None, route_outs: Optional[Sequence[dict]] = None, miss_te=None, miss_w=None,
-            miss_cap: int = 0, miss_count=None, flags: int = 0, events: Optional[Sequence[int]] = None,
-            stream=None):
-    """Forward of len(layers) stacked layers (see strata_moe_forward)."""
-    lib = load_library()
+def _forward_args(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, ws, ws_bytes: int,
+                  resid_out=None, route_outs: Optional[Sequence[dict]] = None, miss_te=None, miss_w=None,
+                  miss_cap: int = 0, miss_count=None, flags: int = 0, events: Optional[Sequence[int]] = None,
+                  stream=None) -> tuple:
     L = len(layers)
     c_layers = (Layer * L)(*[ly.as_c() for ly in layers])
     c_ro = None
@@ -199,9 +197,33 @@ def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_la
     if events:
         ev = (ctypes.c_void_p * len(events))(*events)
         n_ev = len(events) // 2
-    _check(lib.strata_moe_forward(ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last),
-                                  _ptr(resid_out), c_ro, _ptr(miss_te), _ptr(miss_w), miss_cap, _ptr(miss_count),
-                                  _ptr(ws), ws_bytes, ev, n_ev, _stream(stream)))
+    return (ctypes.byref(sh), c_layers, L, _ptr(x), xdtype, T, flags, _ptr(y_last), _ptr(resid_out), c_ro,
+            _ptr(miss_te), _ptr(miss_w), miss_cap, _ptr(miss_count), _ptr(ws), ws_bytes, ev, n_ev, _stream(stream))
+
+
+def forward(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, ws, ws_bytes: int,
+            resid_out=None, route_outs: Optional[Sequence[dict]] = None, miss_te=None, miss_w=None,
+            miss_cap: int = 0, miss_count=None, flags: int = 0, events: Optional[Sequence[int]] = None,
+            stream=None):
+    """Forward of len(layers) stacked layers (see strata_moe_forward)."""
+    lib = load_library()
+    _check(lib.strata_moe_forward(*_forward_args(sh, layers, x, xdtype, T, y_last, ws, ws_bytes, resid_out,
+                                                 route_outs, miss_te, miss_w, miss_cap, miss_count, flags, events,
+                                                 stream)))
+
+
+class PreparedForward:
+    """A forward call whose arguments are marshalled once (same arguments as
+    forward()); calling it enqueues the call again with the same pointers,
+    so a loop of calls spends its host time in the library, not in argument
+    marshalling."""
+
+    def __init__(self, *args, **kwargs):
+        self._fn = load_library().strata_moe_forward
+        self._args = _forward_args(*args, **kwargs)
+
+    def __call__(self):
+        _check(self._fn(*self._args))
 
 
 def forward_noalloc(sh: Shape, layers: Sequence[LayerData], x, xdtype: int, T: int, y_last, resid_out=None,
