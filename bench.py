@@ -220,7 +220,7 @@ def bench_workload(name, args, res, dev, probes, steps, warmup):
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
     resid = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    names = brx.kernel_names(sh, T)
+    names = brx.kernel_names(sh, T, depth)   # kernel groups of one call, in launch order
     miss = {}
     if res.mask is not None:   # miss list of every (token, non-resident pick); T*k entries never overflow
         cap = T * k
@@ -281,20 +281,20 @@ def bench_workload(name, args, res, dev, probes, steps, warmup):
     tokens_per_s = T * calls * steps / (total_ms / 1e3)
 
     # ---- per-kernel durations: library-recorded HIP events around each
-    # kernel group, same steps (the i-th group of layer l is group l*nk + i)
+    # kernel group of a call, same steps (averaged over groups of one name)
     nk = len(names)
     kern_us = {n: [] for n in names}
     if not args.profile_only:
         hip = _Hip()
-        ev_calls = min(steps * calls, max(1, 20000 // (2 * nk * depth)))
-        evs = [[hip.event() for _ in range(2 * nk * depth)] for _ in range(ev_calls)]
+        ev_calls = min(steps * calls, max(1, 20000 // (2 * nk)))
+        evs = [[hip.event() for _ in range(2 * nk)] for _ in range(ev_calls)]
         torch.cuda.synchronize()
         for j in range(ev_calls):   # one forward call per event set
             step(warmup + j // calls, events=evs[j], call=j % calls)
         torch.cuda.synchronize()
         for j in range(ev_calls):
-            for g in range(nk * depth):
-                kern_us[names[g % nk]].append(hip.elapsed_ms(evs[j][2 * g], evs[j][2 * g + 1]) * 1e3)
+            for g in range(nk):
+                kern_us[names[g]].append(hip.elapsed_ms(evs[j][2 * g], evs[j][2 * g + 1]) * 1e3)
         for row in evs:
             for e in row:
                 hip.destroy(e)

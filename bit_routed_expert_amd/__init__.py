@@ -94,7 +94,7 @@ def load_library(path: str = LIB_PATH):
     lib.strata_moe_resident_topn.restype = ctypes.c_int
     lib.strata_moe_resident_topn.argtypes = [vp, i32, i32, vp, vp]
     lib.strata_moe_kernel_names.restype = i32
-    lib.strata_moe_kernel_names.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(ctypes.c_char_p), i32]
+    lib.strata_moe_kernel_names.argtypes = [ctypes.POINTER(Shape), i32, i32, ctypes.POINTER(ctypes.c_char_p), i32]
     lib.strata_status_str.restype = ctypes.c_char_p
     lib.strata_status_str.argtypes = [ctypes.c_int]
     lib.strata_probe_hbm_read.restype = ctypes.c_int
@@ -161,9 +161,12 @@ def workspace_bytes(sh: Shape, T: int, L: int = 1) -> int:
     return n
 
 
-def kernel_names(sh: Shape, T: int) -> list:
-    arr = (ctypes.c_char_p * 16)()
-    n = load_library().strata_moe_kernel_names(ctypes.byref(sh), T, arr, 16)
+def kernel_names(sh: Shape, T: int, L: int = 1) -> list:
+    """Kernel groups of an L-layer forward call with T tokens, in launch order."""
+    lib = load_library()
+    n = lib.strata_moe_kernel_names(ctypes.byref(sh), T, L, None, 0)
+    arr = (ctypes.c_char_p * max(n, 1))()
+    n = lib.strata_moe_kernel_names(ctypes.byref(sh), T, L, arr, n)
     return [arr[i].decode() for i in range(n)]
 
 

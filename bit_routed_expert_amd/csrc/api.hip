@@ -57,6 +57,13 @@ bool small_path(const strata_moe_shape &s, int64_t T) {
     return T <= SMALL_T && (size_t)T * s.d_model * sizeof(float) <= 64 * 1024;
 }
 
+// Decode-path batches of 2..8 tokens (the item-major expert kernels, whose
+// outputs a separate combine sums): in a stack, a layer's combine is folded
+// into the next layer's router kernel.
+bool fuse_combine(const strata_moe_shape &s, int64_t T) {
+    return small_path(s, T) && !strata::gemv_one_token((int)T, s.n_experts, s.top_k, s.d_model, s.d_ff);
+}
+
 // Work items: an expert's slots in pairs (decode path: at most one per
 // pick, plus the shared expert's), else tiles of up to GEMM_BM tokens per
 // resident expert with picks plus the shared expert's.
@@ -75,7 +82,7 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.max_items = max_items_for(s, T);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-    l.z = take(sizeof(float) * T * E * (sp ? 1 : route_logit_splits((int)d)));
+    l.z = take(sizeof(float) * T * E * (sp ? route_logit_planes((int)d) : route_logit_splits((int)d)));
     l.idx = take(4 * T * k);
     l.gate = take(4 * T * k);
     l.counts = take(4 * E);
@@ -125,6 +132,7 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.T = T;
     a.z = (float *)(ws + l.z);
     a.zsplit = small_path(s, T) ? 1 : route_logit_splits(s.d_model);
+    a.zplanes = 1;
     a.idx = (int32_t *)(ws + l.idx);
     a.gate = (float *)(ws + l.gate);
     a.counts = (int32_t *)(ws + l.counts);
@@ -216,17 +224,33 @@ const char *strata_status_str(strata_status s) {
     }
 }
 
-int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max) {
+int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, int32_t L, const char **names,
+                                int32_t max) {
     static const char *one[] = {"route_logits", "route_gemv_gateup", "gemv_down_combine"};
     static const char *small[] = {"route_logits", "route_gemv_gateup", "gemv_down", "combine"};
     static const char *large[] = {"gemm_prep", "route_logits", "route_topk", "route_permute",
                                   "gemm_gateup", "gemm_down", "combine"};   // route_permute: three kernels
-    if (check_shape(shape) != STRATA_OK) return 0;
-    const bool sp = small_path(*shape, T);
-    const bool t1 = sp && gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff);
-    const char **src = sp ? (t1 ? one : small) : large;
-    const int n = sp ? (t1 ? 3 : 4) : 7;
-    for (int i = 0; i < n && i < max; ++i) names[i] = src[i];
+    if (check_shape(shape) != STRATA_OK || T < 1 || L < 1) return 0;
+    int n = 0;
+    auto put = [&](const char *s) {
+        if (n < max) names[n] = s;
+        ++n;
+    };
+    if (!small_path(*shape, T)) {
+        for (int l = 0; l < L; ++l)
+            for (const char *s : large) put(s);
+    } else if (gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff)) {
+        for (int l = 0; l < L; ++l)
+            for (const char *s : one) put(s);
+    } else {
+        // layer l > 0 of a stack: the previous layer's combine and this router in one kernel
+        for (int l = 0; l < L; ++l) {
+            put(l == 0 || L == 1 ? small[0] : "combine_route_logits");
+            put(small[1]);
+            put(small[2]);
+        }
+        put(small[3]);
+    }
     return n;
 }
 
@@ -373,6 +397,12 @@ strata_status forward_impl(const strata_moe_shape *shape, const strata_moe_layer
     char *w = (char *)ws;
     Recorder rec{events, n_events, 0, (hipStream_t)stream};
 
+    // T = 2..8 stacks: the combine of layer l runs inside layer l+1's router
+    // kernel (same arithmetic), so only the last layer launches a combine
+    const bool fuse = L > 1 && !cp && fuse_combine(*shape, T);
+    const void *px = nullptr;          // previous layer's input and mask
+    int px_bf16 = 0;
+    const uint32_t *pmask = nullptr;
     for (int l = 0; l < L; ++l) {
         LayerArgs a;
         fill_common(a, *shape, lay, w, T);
@@ -403,8 +433,20 @@ strata_status forward_impl(const strata_moe_shape *shape, const strata_moe_layer
         a.out = (l == L - 1) ? y_last : (float *)(w + lay.out);
         a.x_next = (l == L - 1) ? resid_out : (float *)(w + (l % 2 ? lay.xres1 : lay.xres0));
         const bool co = cp && a.mask;   // this layer's misses go to the host
-        st = route_layer(a, *shape, T, rec);
-        if (st != STRATA_OK) return st;
+        if (fuse && l > 0) {
+            a.px = px;
+            a.px_is_bf16 = px_bf16;
+            a.pmask = pmask;
+            a.x_cur = (float *)const_cast<void *>(a.x);
+            a.zplanes = route_logit_planes(shape->d_model);
+            RUN(launch_route_combine_small(a, rec.s));
+        } else {
+            st = route_layer(a, *shape, T, rec);
+            if (st != STRATA_OK) return st;
+        }
+        px = a.x;
+        px_bf16 = a.x_is_bf16;
+        pmask = a.mask;
         if (small_path(*shape, T)) {
             // the gate/up kernel completes the routing and the miss list
             if (gemv_one_token(T, shape->n_experts, shape->top_k, shape->d_model, shape->d_ff)) {
@@ -415,7 +457,7 @@ strata_status forward_impl(const strata_moe_shape *shape, const strata_moe_layer
                 RUN(launch_gemv_gateup_multi(a, (int)lay.max_items, rec.s));
                 if (co && (st = coproc_copy_out(*cp, a, rec.s)) != STRATA_OK) return st;
                 RUN(launch_gemv_down_multi(a, (int)lay.max_items, rec.s));
-                RUN(launch_combine(a, rec.s));
+                if (!fuse || l == L - 1) RUN(launch_combine(a, rec.s));
             }
         } else {
             if (co && (st = coproc_copy_out(*cp, a, rec.s)) != STRATA_OK) return st;

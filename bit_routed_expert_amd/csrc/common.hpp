@@ -90,31 +90,56 @@ __device__ __forceinline__ void digit_words(const int X[8], uint32_t word[6]) {
     }
 }
 
-// 1 / sqrt(mean(x_t^2) + eps) of token t (1 when the layer does not
-// normalise); whole block, red = LDS scratch of blockDim/64 floats.
-template <typename Args>
-__device__ float token_inv_rms(const Args &a, int t, float *red) {
-    if (!a.normalize) return 1.f;
-    const int d = a.d, nth = blockDim.x, th = threadIdx.x;
+// 1 / sqrt(mean(x^2) + eps) of one row of d values (1 when the layer does
+// not normalise), ld(i) = value i of the row.  Threads 0..nth-1 of the
+// block (nth <= blockDim.x, a multiple of 64) accumulate, all threads take
+// the barriers; red = LDS scratch of nth/64 floats.  The result depends on
+// nth, not on the block size or on where the row is read from.
+template <typename Load>
+__device__ float row_inv_rms(int d, int normalize, float *red, int nth, Load ld) {
+    if (!normalize) return 1.f;
+    const int th = threadIdx.x;
     float ss = 0.f;
-    for (int i0 = 0; i0 < d; i0 += 8 * nth) {  // 8 independent loads in flight per pass
-        float xv[8];
+    if (th < nth) {
+        for (int i0 = 0; i0 < d; i0 += 8 * nth) {  // 8 independent loads in flight per pass
+            float xv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const size_t o = (size_t)t * d + min(i0 + th + j * nth, d - 1);
-            xv[j] = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+            for (int j = 0; j < 8; ++j) xv[j] = ld(min(i0 + th + j * nth, d - 1));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = (i0 + th + j * nth < d) ? xv[j] : 0.f;
+                ss = fmaf(v, v, ss);
+            }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += (i0 + th + j * nth < d) ? xv[j] * xv[j] : 0.f;
     }
     ss = wave_sum(ss);
     __syncthreads();
-    if ((th & 63) == 0) red[th >> 6] = ss;
+    if ((th & 63) == 0 && th < nth) red[th >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
     for (int w = 0; w < nth / 64; ++w) tot += red[w];
     __syncthreads();
     return 1.f / sqrtf(tot / (float)d + RMS_EPS);
+}
+
+// Value i of token t's layer input as fp32.
+template <typename Args> __device__ __forceinline__ float x_value(const Args &a, int t, int i) {
+    const size_t o = (size_t)t * a.d + i;
+    return a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+}
+
+// Inverse RMS of token t's layer input, over the whole block.
+template <typename Args>
+__device__ float token_inv_rms(const Args &a, int t, float *red) {
+    return row_inv_rms(a.d, a.normalize, red, (int)blockDim.x, [&](int i) { return x_value(a, t, i); });
+}
+
+// Combine step of one pick: s += g * y, component by component (fma).
+__device__ __forceinline__ void combine_acc(float4 &s, float g, const float4 &y) {
+    s.x = fmaf(g, y.x, s.x);
+    s.y = fmaf(g, y.y, s.y);
+    s.z = fmaf(g, y.z, s.z);
+    s.w = fmaf(g, y.w, s.w);
 }
 
 // Work item of the expert kernels: consecutive slots of one expert (up to
@@ -142,6 +167,7 @@ struct LayerArgs {
     // routing state (internal)
     float *z;            // [T][E] logits; larger T: [zsplit][T][E] partial sums over column ranges
     int zsplit;          // column ranges of the larger-T router (1 on the decode path)
+    int zplanes;         // decode path: planes [zplanes][T][E] of z, added in order (1, or one per 256 columns)
     int32_t *idx;        // [T][k]
     float *gate;         // [T][k]
     int32_t *counts;     // [E]
@@ -180,6 +206,14 @@ struct LayerArgs {
     float *out;          // [T][d] layer output
     float *x_next;       // [T][d] residual stream after this layer (nullable)
     int route_only;
+    // decode path, a layer after the first: the previous layer's combine runs
+    // inside this layer's router kernel.  px: that layer's input (bf16 or
+    // fp32), pmask: its resident mask; idx, pos, gate and Y still hold its
+    // routing and expert outputs; x_cur: where this layer's input (= a.x) is written.
+    const void *px;
+    int px_is_bf16;
+    const uint32_t *pmask;
+    float *x_cur;
 };
 
 // Optional HIP events around the next kernels of the calling thread: the
@@ -205,6 +239,9 @@ strata_status hip_status(hipError_t e);
 // Launchers (one file each); return hipGetLastError() of their launches.
 hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s);
 hipError_t launch_route_small_finish(const LayerArgs &a, hipStream_t s);
+// previous layer's combine + this layer's router (T <= 8, a layer after the first)
+hipError_t launch_route_combine_small(const LayerArgs &a, hipStream_t s);
+int route_logit_planes(int d);   // planes of z that kernel writes (one per 256 columns)
 hipError_t launch_gemv_gateup_small(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_gemv_gateup_multi(const LayerArgs &a, int max_items, hipStream_t s);
 hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s);

@@ -23,8 +23,10 @@ constexpr size_t LDS_LIMIT = 64 * 1024;
 // per 256-column group an exponent E with max|u| * 2^E inside the 4-digit
 // range, X = rint(u * 2^E), and its balanced base-16 digits packed 8 columns
 // per word (nibble n of word (unit U, plane p, i) = digit p of column 32U+8i+n).
-// Runs on one block of `nth` threads (multiple of 64).
-__device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/64 floats*/, float inv) {
+// Runs on one block (any multiple of 64 threads); ld(i) = value i of the
+// token's row as fp32.
+template <typename Load>
+__device__ void prep_token_row(const LayerArgs &a, int t, float inv, Load ld) {
     const int d = a.d, nth = blockDim.x, th = threadIdx.x;
     const int nchunk = d / 8;  // 8 columns per chunk
     const int Q = d / 128;
@@ -36,11 +38,7 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
         float u[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-            float xv = 0.f;
-            if (valid) {
-                size_t i = (size_t)t * d + c * 8 + n;
-                xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
-            }
+            const float xv = valid ? ld(c * 8 + n) : 0.f;
             u[n] = xv * inv;
         }
         float m = 0.f;
@@ -71,10 +69,10 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
             if ((c & 31) == 0) a.xscl[(size_t)t * G + c / 32] = ldexpf(1.f, -E);
         }
     }
-    (void)red;
 }
-
-// Inverse RMS of token t's row (1 when the layer input is not normalised).
+__device__ void prep_token(const LayerArgs &a, int t, float inv) {
+    prep_token_row(a, t, inv, [&](int i) { return x_value(a, t, i); });
+}
 
 
 // ------------------------------------------------------ decode-size route
@@ -84,8 +82,46 @@ __device__ void prep_token(const LayerArgs &a, int t, float *red /*lds, >= nth/6
 // inverse RMS and (unless routing only) its input digit planes.  The top-k
 // is taken afterwards by every consumer block from z (a few KB), so no block
 // waits on another inside this kernel.
-constexpr int RS_WAVES = 4;   // router rows per block
-constexpr int RS_MAXJ = 8;    // float4 per lane per 2048-column chunk
+//
+// Order of a dot product x . Wr[e] (route_combine_small_kernel computes the
+// same sums one 256-column chunk per block, so a stack of layers gets the
+// logits of single-layer calls bit for bit): the columns are cut into
+// 256-column chunks; lane s (0..7) of an 8-lane group takes columns
+// 32i + 4s .. 32i + 4s + 3 (i = 0..7) of one chunk as one chain of fmas; the
+// group's 8 partials are added in pairs, then quads, then halves (DPP, the
+// same value in all 8 lanes); the chunk sums are added to 0 in chunk order.
+constexpr int RS_WAVES = 4;     // router rows per block
+constexpr int RS_CHUNK = 256;   // columns per chunk
+
+template <typename XF>
+__device__ __forceinline__ float chunk_part(const float4 (&w)[8], int ni, XF xf) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i < ni) {
+            const float4 x = xf(i);
+            acc = fmaf(w[i].x, x.x, acc);
+            acc = fmaf(w[i].y, x.y, acc);
+            acc = fmaf(w[i].z, x.z, acc);
+            acc = fmaf(w[i].w, x.w, acc);
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float group8_sum(float v) {
+#define G8_DPP(CTRL) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false))
+    v += G8_DPP(0xB1);    // quad_perm [1,0,3,2]
+    v += G8_DPP(0x4E);    // quad_perm [2,3,0,1]
+    v += G8_DPP(0x141);   // row_half_mirror: quad 0 <-> quad 1 of each 8 lanes
+#undef G8_DPP
+    return v;
+}
+
+// LDS place of value v of the staged T x d rows: each 128-value block of an
+// odd 256-value block is rotated by 32, so the 8 lane groups' 128-byte
+// reads of one step fall on both halves of the banks.
+__device__ __forceinline__ int xrot(int v) { return (v & ~127) | ((v + ((v >> 3) & 32)) & 127); }
 
 template <int XBF16>
 __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
@@ -97,22 +133,23 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
         const int t = blockIdx.x - nrow_blocks;
         const float inv = token_inv_rms(a, t, lds);
         if (th == 0) a.inv_rms[t] = inv;
-        if (!a.route_only) prep_token(a, t, nullptr, inv);
+        if (!a.route_only) prep_token(a, t, inv);
         return;
     }
     const int e = blockIdx.x * RS_WAVES + wave;
     const float *wrow = a.Wr + (size_t)(e < E ? e : 0) * d;
-    float *xs = lds;  // [T][d]
+    const int g = lane >> 3, s4 = 4 * (lane & 7);
+    float *xs = lds;  // [T][d], places by xrot
     float zacc[CHUNK_TOK];
 #pragma unroll
     for (int t = 0; t < CHUNK_TOK; ++t) zacc[t] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += 64 * 4 * RS_MAXJ) {
-        float4 wv[RS_MAXJ];
+    for (int c0 = 0; c0 < d; c0 += 8 * RS_CHUNK) {
+        const int cb = c0 + RS_CHUNK * g;                 // this lane group's chunk
+        const int ni = min(8, max(0, (d - cb) / 32));     // its 32-column steps inside d
+        float4 wv[8];
 #pragma unroll
-        for (int j = 0; j < RS_MAXJ; ++j) {
-            const int i = c0 + lane * 4 + 256 * j;
-            wv[j] = (e < E && i < d) ? *(const float4 *)(wrow + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int j = 0; j < 8; ++j)
+            wv[j] = (e < E && j < ni) ? *(const float4 *)(wrow + cb + 32 * j + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
         if (c0 == 0) {
             // the T rows of x into LDS as fp32: 16-byte loads, eight per thread in flight
             constexpr int PER = XBF16 ? 8 : 4;   // values per 16-byte chunk
@@ -130,40 +167,147 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
                     if (c < nch) {
                         const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
                         if (XBF16) {
-                            float4 *dst = (float4 *)(xs + 8 * c);
+                            float4 *dst = (float4 *)(xs + xrot(8 * c));
                             dst[0] = make_float4(__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xFFFF0000u),
                                                  __uint_as_float(q[1] << 16), __uint_as_float(q[1] & 0xFFFF0000u));
                             dst[1] = make_float4(__uint_as_float(q[2] << 16), __uint_as_float(q[2] & 0xFFFF0000u),
                                                  __uint_as_float(q[3] << 16), __uint_as_float(q[3] & 0xFFFF0000u));
                         } else {
-                            *(float4 *)(xs + 4 * c) = make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]),
-                                                                  __uint_as_float(q[2]), __uint_as_float(q[3]));
+                            *(float4 *)(xs + xrot(4 * c)) = make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]),
+                                                                        __uint_as_float(q[2]), __uint_as_float(q[3]));
                         }
                     }
                 }
             }
             __syncthreads();
         }
+        const int nch = min(8, (d - c0 + RS_CHUNK - 1) / RS_CHUNK);   // chunks of this pass
 #pragma unroll
         for (int t = 0; t < CHUNK_TOK; ++t) {
             if (t < T) {
-                float acc = 0.f;
+                const int rb = t * d + cb + s4;
+                float p = chunk_part(wv, ni, [&](int i) { return *(const float4 *)(xs + xrot(rb + 32 * i)); });
+                p = group8_sum(p);
 #pragma unroll
-                for (int j = 0; j < RS_MAXJ; ++j) {
-                    const int i = c0 + lane * 4 + 256 * j;
-                    if (i < d) {
-                        const float4 xv = *(const float4 *)(xs + t * d + i);
-                        acc += wv[j].x * xv.x + wv[j].y * xv.y + wv[j].z * xv.z + wv[j].w * xv.w;
-                    }
-                }
-                zacc[t] += wave_sum_dpp(acc);   // complete in lanes 48..63
+                for (int c = 0; c < 8; ++c)
+                    if (c < nch)
+                        zacc[t] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 8 * c));
             }
         }
     }
-    if (lane == 63 && e < E) {
+    if (lane == 0 && e < E) {
 #pragma unroll
         for (int t = 0; t < CHUNK_TOK; ++t)
             if (t < T) a.z[t * E + e] = zacc[t];
+    }
+}
+
+// ------------------------------------- decode-size route after a layer
+// T <= 8, a layer after the first of a stack: the previous layer's combine
+// and this layer's router in one kernel (the combine kernel's launch and
+// the round trip of x through memory go).  Blocks [0, nr * ng): chunk c of
+// router rows 64q .. 64q+63 (c = block mod nr, so the blocks of one chunk
+// share an XCD): the chunk of every token's row x = x_prev + out_prev is
+// formed in LDS exactly as combine_kernel forms it, then each wave dots 8
+// router rows with it (one per 8-lane group, lanes as in
+// route_logits_small_kernel) and writes the chunk sums as plane c of z.
+// Blocks past those: one per token, its whole row x (also written to
+// x_cur), its inverse RMS over 256 threads and its digit planes.
+constexpr int RC_ROWS = 64;   // router rows per block: 8 waves x 8 lane groups
+
+// x_prev + out_prev at columns i .. i+3 of token t; rp, rg: the token's k
+// picks as Y rows (-1 when the expert is not resident) and gates.
+template <int PXBF16>
+__device__ __forceinline__ float4 combine_x(const LayerArgs &a, int t, int i, const int *rp, const float *rg) {
+    const int d = a.d, k = a.k;
+    const float *__restrict__ Y = a.Y;
+    float4 s = *(const float4 *)(Y + ((int64_t)a.T * k + t) * d + i);
+    for (int r0 = 0; r0 < k; r0 += 16) {
+        int pr[16];
+        float4 yv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = r0 + r < k ? rp[r0 + r] : -1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            yv[r] = pr[r] >= 0 ? *(const float4 *)(Y + (int64_t)pr[r] * d + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (pr[r] >= 0) combine_acc(s, rg[r0 + r], yv[r]);
+    }
+    const int64_t row = (int64_t)t * d + i;
+    float4 xv;
+    if (PXBF16) {
+        const uint2 q = *(const uint2 *)((const uint16_t *)a.px + row);
+        xv = make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
+                         __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
+    } else {
+        xv = *(const float4 *)((const float *)a.px + row);
+    }
+    return make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w);
+}
+
+constexpr int RC_ROUTE_WORDS = 2 * CHUNK_TOK * 32;   // staged routing: slots and gates of T*k <= 256 picks
+
+template <int PXBF16>
+__global__ __launch_bounds__(512) void route_combine_small_kernel(LayerArgs a) {
+    extern __shared__ float lds[];
+    const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+    const int d = a.d, T = a.T, E = a.E, k = a.k;
+    const int nr = (d + RS_CHUNK - 1) / RS_CHUNK, ng = (E + RC_ROWS - 1) / RC_ROWS;
+    int *rpos = (int *)lds;                       // [nt*k] Y row of each pick of the previous layer, or -1
+    float *rgate = lds + CHUNK_TOK * 32;          // [nt*k] its gate
+    float *xs = lds + RC_ROUTE_WORDS;             // router blocks: [T][256]; token blocks: [d] + 4 floats
+    const bool router = (int)blockIdx.x < nr * ng;
+    const int c = (int)blockIdx.x % nr;
+    const int t0 = router ? 0 : (int)blockIdx.x - nr * ng;
+    const int nt = router ? T : 1;
+    const int g = lane >> 3, s4 = 4 * (lane & 7);
+    const int e = ((int)blockIdx.x / nr) * RC_ROWS + 8 * wave + g;
+    const int cb = RS_CHUNK * c;
+    const int ni = min(8, max(0, (d - cb) / 32));
+    float4 wv[8];
+    if (router) {
+        const float *wrow = a.Wr + (size_t)(e < E ? e : 0) * d;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            wv[j] = (e < E && j < ni) ? *(const float4 *)(wrow + cb + 32 * j + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int j = th; j < nt * k; j += blockDim.x) {
+        const int r = t0 * k + j;
+        const int ep = a.idx[r];
+        const bool res = !a.pmask || ((a.pmask[ep >> 5] >> (ep & 31)) & 1u);
+        rpos[j] = res ? a.pos[r] : -1;
+        rgate[j] = a.gate[r];
+    }
+    __syncthreads();
+    if (router) {
+        const int w4 = min(RS_CHUNK / 4, (d - cb) / 4);   // float4 columns of this chunk inside d
+        for (int u = th; u < T * (RS_CHUNK / 4); u += blockDim.x) {
+            const int t = u / (RS_CHUNK / 4), q4 = u % (RS_CHUNK / 4);
+            if (q4 < w4)
+                *(float4 *)(xs + RS_CHUNK * t + 4 * q4) = combine_x<PXBF16>(a, t, cb + 4 * q4, rpos + t * k, rgate + t * k);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < CHUNK_TOK; ++t) {
+            if (t < T) {
+                const float *xr = xs + RS_CHUNK * t + s4;
+                float p = chunk_part(wv, ni, [&](int i) { return *(const float4 *)(xr + 32 * i); });
+                p = group8_sum(p);
+                if ((lane & 7) == 0 && e < E) a.z[((size_t)c * T + t) * E + e] = p;
+            }
+        }
+    } else {
+        const int t = t0;
+        for (int u = th; u < d / 4; u += blockDim.x) {
+            const float4 v = combine_x<PXBF16>(a, t, 4 * u, rpos, rgate);
+            *(float4 *)(xs + 4 * u) = v;
+            *(float4 *)(a.x_cur + (size_t)t * d + 4 * u) = v;
+        }
+        __syncthreads();
+        const float inv = row_inv_rms(d, a.normalize, xs + d, 256, [&](int i) { return xs[i]; });
+        if (th == 0) a.inv_rms[t] = inv;
+        prep_token_row(a, t, inv, [&](int i) { return xs[i]; });
     }
 }
 
@@ -510,6 +654,20 @@ hipError_t launch_route_logits_small(const LayerArgs &a, hipStream_t s) {
         STRATA_LAUNCH(route_logits_small_kernel<1>, dim3(blocks), dim3(256), lds, s, a);
     else
         STRATA_LAUNCH(route_logits_small_kernel<0>, dim3(blocks), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+int route_logit_planes(int d) { return (d + RS_CHUNK - 1) / RS_CHUNK; }
+
+hipError_t launch_route_combine_small(const LayerArgs &a, hipStream_t s) {
+    const int nr = route_logit_planes(a.d), ng = (a.E + RC_ROWS - 1) / RC_ROWS;
+    const size_t lds = sizeof(float) * (RC_ROUTE_WORDS + std::max((size_t)a.T * RS_CHUNK, (size_t)a.d + 4));
+    if (lds > LDS_LIMIT || a.T > CHUNK_TOK || a.k > 32 || !a.px || !a.x_cur || a.zplanes != nr)
+        return hipErrorInvalidValue;
+    if (a.px_is_bf16)
+        STRATA_LAUNCH(route_combine_small_kernel<1>, dim3(nr * ng + a.T), dim3(512), lds, s, a);
+    else
+        STRATA_LAUNCH(route_combine_small_kernel<0>, dim3(nr * ng + a.T), dim3(512), lds, s, a);
     return hipGetLastError();
 }
 

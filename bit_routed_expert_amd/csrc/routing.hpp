@@ -116,13 +116,47 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 //   3. Each candidate's rank is the number of larger entries (LDS reads that
 //      every lane shares); rank r < k is pick r.
 // More than TOPK_CAND candidates (many equal values) take the rounds above.
+// planes > 1: z[e] is 0 + z[e] + z[pstride + e] + ... (planes terms, in
+// order), the loads of up to 64 values per lane issued before their adds.
 template <int JM>
 __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
-                                                     uint32_t *cand, int *e_out, float *z_out) {
+                                                     uint32_t *cand, int *e_out, float *z_out, int planes = 1,
+                                                     int pstride = 0) {
     const int lane = threadIdx.x & 63;
     float zv[JM], bv[JM];
+    if (planes == 1) {
 #pragma unroll
-    for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
+        for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < JM; ++j) zv[j] = 0.f;
+        constexpr int NPG = 64 / JM;   // planes per group of loads (64 values per lane)
+        typedef const float __attribute__((address_space(1))) gfloat;
+        int off[JM];
+#pragma unroll
+        for (int j = 0; j < JM; ++j) off[j] = min(lane + 64 * j, E - 1);
+        for (int p0 = 0; p0 < planes; p0 += NPG) {
+            // every load of the group issued, none behind a branch (planes past the
+            // last re-read the last one); only planes < `planes` are added
+            float pv[NPG][JM];
+#pragma unroll
+            for (int p = 0; p < NPG; ++p) {
+                // the plane's base in scalar registers (each half through uint32_t:
+                // readfirstlane returns int, which would sign-extend)
+                const uint64_t b = (uint64_t)(z + (size_t)min(p0 + p, planes - 1) * pstride);
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+                gfloat *zp = (gfloat *)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+                for (int j = 0; j < JM; ++j) pv[p][j] = zp[off[j]];
+            }
+#pragma unroll
+            for (int p = 0; p < NPG; ++p)
+#pragma unroll
+                for (int j = 0; j < JM; ++j)
+                    if (p0 + p < planes) zv[j] += pv[p][j];
+        }
+    }
 #pragma unroll
     for (int j = 0; j < JM; ++j) bv[j] = 0.f;
     if (bias) {
@@ -222,14 +256,15 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
 // Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
 __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float scale, const float *bias,
                                           uint32_t *cand, int32_t *idx_out, float *gate_out, int32_t *idx_out2,
-                                          float *gate_out2, int32_t *idx_lds, float *gate_lds) {
+                                          float *gate_out2, int32_t *idx_lds, float *gate_lds, int planes = 1,
+                                          int pstride = 0) {
     const int lane = threadIdx.x & 63;
     int e;
     float v;
     if (E <= 512)
-        wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v);
+        wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
     else
-        wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v);
+        wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
     const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float p = (lane < k) ? expf(v - top) : 0.f;
     const float s = wave_allsum_f32(p);
@@ -302,7 +337,7 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
     if (th < 32) L.picked[th] = 0;
     for (int t = wave; t < T; t += nw)
         wave_topk(z + t * E, E, k, inv[t], a.bias, L.cand + (wave % SMALL_ROUTE_WAVES) * TOPK_LDS_WORDS, nullptr,
-                  nullptr, nullptr, nullptr, L.sidx + t * k, L.sgate + t * k);
+                  nullptr, nullptr, nullptr, L.sidx + t * k, L.sgate + t * k, a.zplanes, T * E);
     __syncthreads();
     if (th < T * k) {
         const int e = L.sidx[th];

@@ -263,9 +263,15 @@ strata_status strata_moe_forward_coprocess(const strata_moe_shape *shape, const 
                                            size_t ws_bytes, void *host_ws, size_t host_ws_bytes, int32_t n_threads,
                                            void *aux_stream, void *stream);
 
-/* Names of the kernels strata_moe_forward enqueues for one layer, in order,
- * for a token count T; returns how many (<= max) and writes static strings. */
-int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, const char **names, int32_t max);
+/* Names of the kernel groups an L-layer strata_moe_forward call with T tokens
+ * enqueues, in order (the i-th is what events[2i], events[2i+1] bracket):
+ * static strings, the first max of them written to names.  Returns the
+ * number of groups (which may exceed max), 0 for an invalid shape, T < 1 or
+ * L < 1.  For T = 2..8 a stack folds each layer's combine into the next
+ * layer's router kernel ("combine_route_logits"), so only the last layer
+ * ends with "combine": 3L + 1 groups. */
+int32_t strata_moe_kernel_names(const strata_moe_shape *shape, int32_t T, int32_t L, const char **names,
+                                int32_t max);
 
 /* Running expert popularity (the expert cache learns which experts are hot as
  * it is used: wiselychen.com, technique 2 "專家快取與 CPU／GPU 分工"; wiki.nginx.tw,

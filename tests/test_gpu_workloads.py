@@ -302,3 +302,63 @@ def test_mixed_bit_width_stack(name, T):
     G.assert_close(got["y"], refs[-1]["out"], what="last layer output")
     G.assert_close(got["resid"], xl, what="residual")
     assert isinstance(dl[1], brx.LayerData) and dl[1].bits == 2
+
+
+def _mask_words(E, resident):
+    words = np.zeros((E + 31) // 32, np.uint32)
+    for e in np.flatnonzero(resident):
+        words[e >> 5] |= np.uint32(1) << np.uint32(e & 31)
+    return words
+
+
+@pytest.mark.parametrize("E,k,d,f,bits,T,masked", [(16, 2, 384, 128, 3, 2, True), (64, 4, 1024, 256, 2, 8, True),
+                                                    (1024, 8, 2048, 256, 3, 5, False),
+                                                    (512, 10, 2048, 768, 3, 3, True)])
+def test_stack_equals_chained_layer_calls(E, k, d, f, bits, T, masked):
+    """T = 2..8: in a stack each layer's combine runs inside the next layer's
+    router kernel, which forms the logits as one partial sum per 256-column
+    chunk.  Three layers in one call equal three chained one-layer calls bit
+    for bit (output, residual, routing, miss lists), with resident masks
+    that differ per layer, d = 384 (two chunks, the second a half), 1024
+    and 2048, 8 tokens and E > 512; every layer's routing against the
+    oracle's chain, the last output and residual within the bound."""
+    w = synth.Workload(f"fold_E{E}_d{d}_b{bits}", E, k, d, f, bits, T, seed=0x5EED0C00 + E + d + T)
+    rng = np.random.default_rng(0xF01D + E + d)
+    Ls, refs, x0, xl = [], [], None, None
+    for l in range(3):
+        attempt = 0
+        while True:
+            Lr = W.layer_data(w, l, attempt)
+            if l == 0:
+                x0, _ = W.draw_tokens(w, Lr["Wr"], None, range(T), rep=23)
+                xl = synth.bf16_to_f32(x0)
+            u = oracle.layer_input(xl, l)
+            if oracle.topk_margin(oracle.logits(u, Lr["Wr"]), w.top_k).min() >= W.MARGIN:
+                break
+            attempt += 1
+        if masked:
+            Lr["mask"] = _mask_words(E, rng.random(E) < 0.7)
+        r = oracle.moe_layer(bits, E, k, d, f, u, Lr["Wr"], Lr["codes"], Lr["scales"], mask=Lr.get("mask"))
+        Ls.append(Lr)
+        refs.append(r)
+        xl = oracle.residual_add(xl, r["out"])
+    print(f"case fold E={E} k={k} d={d} f={f} bits={bits} T={T} masked={masked}", flush=True)
+    dl = [G.layer_to_dev(Lr) for Lr in Ls]
+    got = G.run_forward(w, dl, G.dev(x0), 0, T)
+    t = _torch()
+    xc, xd = G.dev(x0), 0
+    for l in range(3):
+        one = G.run_forward(w, [dl[l]], xc, xd, T, flags=(1 if l > 0 else 0))
+        for key in one["route"][0]:
+            np.testing.assert_array_equal(one["route"][0][key], got["route"][l][key], err_msg=f"layer {l} {key}")
+        if masked:
+            n = int(one["miss_count"][0])
+            assert n == int(got["miss_count"][l])
+            np.testing.assert_array_equal(one["miss_te"][0][:n], got["miss_te"][l][:n])
+            np.testing.assert_array_equal(one["miss_w"][0][:n], got["miss_w"][l][:n])
+        np.testing.assert_array_equal(got["route"][l]["topk_idx"], refs[l]["idx"], err_msg=f"layer {l} ids")
+        xc, xd = t.from_numpy(one["resid"]).cuda(), 1
+    np.testing.assert_array_equal(one["y"], got["y"])
+    np.testing.assert_array_equal(one["resid"], got["resid"])
+    G.assert_close(got["y"], refs[-1]["out"], what="y_2")
+    G.assert_close(got["resid"], xl, what="x_3")
