@@ -49,7 +49,7 @@ constexpr int SMALL_T = 8;
 
 struct Layout {
     size_t z, idx, gate, counts, offsets, perm, pos, inv_rms, items, n_items, xq, xsum, xscl, hf,
-        xa, sx, ha, hs, bcnt, bmiss, Y, out, xres0, xres1, miss_count, total;
+        xa, sx, ha, hs, bcnt, bmiss, Y, rbits, out, xres0, xres1, miss_count, total;
     int64_t max_items;
 };
 
@@ -104,6 +104,7 @@ Layout layout(const strata_moe_shape &s, int64_t T) {
     l.bcnt = take(4 * nb * E);
     l.bmiss = take(4 * nb);
     l.Y = take(sizeof(float) * slots * d);
+    l.rbits = take(4 * T);
     l.out = take(sizeof(float) * T * d);
     l.xres0 = take(sizeof(float) * T * d);
     l.xres1 = take(sizeof(float) * T * d);
@@ -147,6 +148,7 @@ void fill_common(LayerArgs &a, const strata_moe_shape &s, const Layout &l, char 
     a.xscl = (float *)(ws + l.xscl);
     a.hf = (float *)(ws + l.hf);
     a.Y = (float *)(ws + l.Y);
+    a.rbits = (int32_t *)(ws + l.rbits);
     a.xa = (uint16_t *)(ws + l.xa);
     a.sx = (float *)(ws + l.sx);
     a.ha = (uint16_t *)(ws + l.ha);
@@ -413,6 +415,7 @@ strata_status forward_impl(const strata_moe_shape *shape, const strata_moe_layer
         a.scales = ly.scales;
         a.mask = ly.resident_mask;
         a.bits = ly.bits ? ly.bits : shape->bits;   // the workspace layout does not depend on it
+        a.ytok = fuse_combine(*shape, T) ? 1 : 0;   // item-major down kernel: Y rows in token order
         if (l == 0) {
             a.x = x;
             a.x_is_bf16 = xdtype == STRATA_X_BF16;

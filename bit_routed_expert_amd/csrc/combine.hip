@@ -16,8 +16,11 @@ constexpr int KB = 16;          // picks gathered per batch (top_k <= 32: at mos
 constexpr int CB_COLS = 1024;   // columns per block (4 per thread)
 
 // One block per (token, 1024-column segment): the token's routing is
-// block-uniform, every thread gathers 4 columns of the picked rows.
-template <int XBF16>
+// block-uniform, every thread gathers 4 columns of the picked rows.  YTOK:
+// Y rows in token order (pick r of token t at row t*k + r) and residency
+// from rbits, so the rows load with the gates in one round trip; else the
+// rows sit at the picks' slots (pos) and residency comes from the mask.
+template <int XBF16, int YTOK>
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     const int d = a.d, k = a.k, T = a.T;
     const int segs = (d + CB_COLS - 1) / CB_COLS;
@@ -27,6 +30,7 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     const float *__restrict__ Y = a.Y;
     const int64_t row = (int64_t)t * d + i;
     float4 s = *(const float4 *)(Y + ((int64_t)T * k + t) * d + i);
+    const uint32_t rb = (YTOK && a.mask) ? (uint32_t)a.rbits[t] : 0xFFFFFFFFu;
     for (int r0 = 0; r0 < k; r0 += KB) {
         int pr[KB];
         float gr[KB];
@@ -35,10 +39,17 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
             pr[r] = -1;
             gr[r] = 0.f;
             if (r0 + r < k) {
-                const int e = a.idx[t * k + r0 + r];
-                if (!a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u)) {
-                    pr[r] = a.pos[t * k + r0 + r];
-                    gr[r] = a.gate[t * k + r0 + r];
+                if (YTOK) {
+                    if ((rb >> (r0 + r)) & 1u) {
+                        pr[r] = t * k + r0 + r;
+                        gr[r] = a.gate[t * k + r0 + r];
+                    }
+                } else {
+                    const int e = a.idx[t * k + r0 + r];
+                    if (!a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u)) {
+                        pr[r] = a.pos[t * k + r0 + r];
+                        gr[r] = a.gate[t * k + r0 + r];
+                    }
                 }
             }
         }
@@ -104,10 +115,17 @@ hipError_t launch_add_rows(const LayerArgs &a, const float *add, hipStream_t s) 
 
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s) {
     const int blocks = a.T * ((a.d + CB_COLS - 1) / CB_COLS);
-    if (a.x_is_bf16)
-        STRATA_LAUNCH(combine_kernel<1>, dim3(blocks), dim3(256), 0, s, a);
-    else
-        STRATA_LAUNCH(combine_kernel<0>, dim3(blocks), dim3(256), 0, s, a);
+    if (a.ytok) {
+        if (a.x_is_bf16)
+            STRATA_LAUNCH((combine_kernel<1, 1>), dim3(blocks), dim3(256), 0, s, a);
+        else
+            STRATA_LAUNCH((combine_kernel<0, 1>), dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        if (a.x_is_bf16)
+            STRATA_LAUNCH((combine_kernel<1, 0>), dim3(blocks), dim3(256), 0, s, a);
+        else
+            STRATA_LAUNCH((combine_kernel<0, 0>), dim3(blocks), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -194,7 +194,10 @@ struct LayerArgs {
     int32_t *xsum;
     float *xscl;
     float *hf;           // [slots][f] SwiGLU activation h of each slot (GEMV path)
-    float *Y;            // [slots][d] expert outputs (larger T)
+    float *Y;            // [slots][d] expert outputs: row = slot, or with ytok row t*k + r for pick r of
+                         // token t (the shared expert's rows stay at slot T*k + t)
+    int ytok;            // decode path, T >= 2: Y rows in token order (combines read them without pos)
+    int32_t *rbits;      // [T] bit r set when pick r of token t is resident (written when a mask is given)
     // GEMM path: bf16 hi/lo activations, columns permuted inside each
     // 128-column step, and their sums over each step (x) or 32-feature group (h)
     uint16_t *xa;        // [2][T][d]

@@ -686,7 +686,7 @@ __host__ __device__ inline int down_multi_lds_words(int f, int R) {
 template <int BITS, int NT, int UPLM>
 __device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkItem &it, const UTile<BITS, UPLM> *wt,
                                                  int R, int Q, int row0, const uint32_t *dig, int dstride,
-                                                 const int *hsum, const float *hscl) {
+                                                 const int *hsum, const float *hscl, const int *yrow) {
     const int lane = threadIdx.x & 63, units = a.f / 32, upl = units / (64 / R);
 #pragma unroll
     for (int q = 0; q < DN_QMAX; ++q) {
@@ -696,7 +696,7 @@ __device__ __forceinline__ void down_multi_tiles(const LayerArgs &a, const WorkI
                                            TOK_IDENTITY, res);
         if (lane < R) {
 #pragma unroll
-            for (int j = 0; j < NT; ++j) a.Y[(size_t)(it.slot0 + j) * a.d + row0 + q * R + lane] = res[j];
+            for (int j = 0; j < NT; ++j) a.Y[(size_t)yrow[j] * a.d + row0 + q * R + lane] = res[j];
         }
     }
 }
@@ -710,6 +710,14 @@ __global__ __launch_bounds__(DN_THREADS) void gemv_down_multi_kernel(LayerArgs a
     const int item = blockIdx.x / chunks;   // < max_items: the list slot exists
     const WorkItem it = a.items[item];      // read together with the count (one round trip)
     if (item >= *a.n_items) return;
+    // Y row of each slot (token order: pick r of token t at t*k + r); needed
+    // only by the stores at the end, so its load overlaps the code stream
+    int yrow[ITEM_TOK];
+#pragma unroll
+    for (int j = 0; j < ITEM_TOK; ++j) {
+        const int sl = it.slot0 + min(j, it.ntok - 1);
+        yrow[j] = (a.ytok && sl < a.T * a.k) ? a.perm[sl] : sl;
+    }
     const int row0 = (blockIdx.x % chunks) * rows_blk + wave * Q * R;
     // loads in the order they are used: this thread's h chunk, then the code
     // tiles (all unconditional, so each wait covers only what it needs)
@@ -771,8 +779,8 @@ __global__ __launch_bounds__(DN_THREADS) void gemv_down_multi_kernel(LayerArgs a
     // products start as soon as its own loads land
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_s_barrier();
-    if (it.ntok == 1) down_multi_tiles<BITS, 1, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
-    else down_multi_tiles<BITS, 2, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl);
+    if (it.ntok == 1) down_multi_tiles<BITS, 1, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl, yrow);
+    else down_multi_tiles<BITS, 2, UPLM>(a, it, wt, R, Q, row0, dig, dstride, hsum, hscl, yrow);
 }
 
 // ------------------------------------------------------------- launchers

@@ -215,24 +215,28 @@ __global__ __launch_bounds__(256) void route_logits_small_kernel(LayerArgs a) {
 // x_cur), its inverse RMS over 256 threads and its digit planes.
 constexpr int RC_ROWS = 64;   // router rows per block: 8 waves x 8 lane groups
 
-// x_prev + out_prev at columns i .. i+3 of token t; rp, rg: the token's k
-// picks as Y rows (-1 when the expert is not resident) and gates.
+// x_prev + out_prev at columns i .. i+3 of token t, as combine_kernel
+// forms them from rows in token order: the shared expert's row, then
+// gate * row t*k + r of each resident pick in r order (fma), added to x.
+// Every load is independent of the others (one round trip).
 template <int PXBF16>
-__device__ __forceinline__ float4 combine_x(const LayerArgs &a, int t, int i, const int *rp, const float *rg) {
+__device__ __forceinline__ float4 combine_x(const LayerArgs &a, int t, int i) {
     const int d = a.d, k = a.k;
     const float *__restrict__ Y = a.Y;
     float4 s = *(const float4 *)(Y + ((int64_t)a.T * k + t) * d + i);
+    const uint32_t rb = a.pmask ? (uint32_t)a.rbits[t] : 0xFFFFFFFFu;
     for (int r0 = 0; r0 < k; r0 += 16) {
-        int pr[16];
+        float gr[16];
         float4 yv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = r0 + r < k ? rp[r0 + r] : -1;
+        for (int r = 0; r < 16; ++r) {
+            const bool on = r0 + r < k && ((rb >> (r0 + r)) & 1u);
+            gr[r] = on ? a.gate[t * k + r0 + r] : 0.f;
+            yv[r] = on ? *(const float4 *)(Y + (int64_t)(t * k + r0 + r) * d + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            yv[r] = pr[r] >= 0 ? *(const float4 *)(Y + (int64_t)pr[r] * d + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (pr[r] >= 0) combine_acc(s, rg[r0 + r], yv[r]);
+            if (r0 + r < k && ((rb >> (r0 + r)) & 1u)) combine_acc(s, gr[r], yv[r]);
     }
     const int64_t row = (int64_t)t * d + i;
     float4 xv;
@@ -246,46 +250,29 @@ __device__ __forceinline__ float4 combine_x(const LayerArgs &a, int t, int i, co
     return make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w);
 }
 
-constexpr int RC_ROUTE_WORDS = 2 * CHUNK_TOK * 32;   // staged routing: slots and gates of T*k <= 256 picks
-
 template <int PXBF16>
 __global__ __launch_bounds__(512) void route_combine_small_kernel(LayerArgs a) {
     extern __shared__ float lds[];
     const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
-    const int d = a.d, T = a.T, E = a.E, k = a.k;
+    const int d = a.d, T = a.T, E = a.E;
     const int nr = (d + RS_CHUNK - 1) / RS_CHUNK, ng = (E + RC_ROWS - 1) / RC_ROWS;
-    int *rpos = (int *)lds;                       // [nt*k] Y row of each pick of the previous layer, or -1
-    float *rgate = lds + CHUNK_TOK * 32;          // [nt*k] its gate
-    float *xs = lds + RC_ROUTE_WORDS;             // router blocks: [T][256]; token blocks: [d] + 4 floats
+    float *xs = lds;   // router blocks: [T][256]; token blocks: [d] + 4 floats
     const bool router = (int)blockIdx.x < nr * ng;
     const int c = (int)blockIdx.x % nr;
-    const int t0 = router ? 0 : (int)blockIdx.x - nr * ng;
-    const int nt = router ? T : 1;
     const int g = lane >> 3, s4 = 4 * (lane & 7);
     const int e = ((int)blockIdx.x / nr) * RC_ROWS + 8 * wave + g;
     const int cb = RS_CHUNK * c;
     const int ni = min(8, max(0, (d - cb) / 32));
-    float4 wv[8];
     if (router) {
+        float4 wv[8];
         const float *wrow = a.Wr + (size_t)(e < E ? e : 0) * d;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             wv[j] = (e < E && j < ni) ? *(const float4 *)(wrow + cb + 32 * j + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    for (int j = th; j < nt * k; j += blockDim.x) {
-        const int r = t0 * k + j;
-        const int ep = a.idx[r];
-        const bool res = !a.pmask || ((a.pmask[ep >> 5] >> (ep & 31)) & 1u);
-        rpos[j] = res ? a.pos[r] : -1;
-        rgate[j] = a.gate[r];
-    }
-    __syncthreads();
-    if (router) {
         const int w4 = min(RS_CHUNK / 4, (d - cb) / 4);   // float4 columns of this chunk inside d
         for (int u = th; u < T * (RS_CHUNK / 4); u += blockDim.x) {
             const int t = u / (RS_CHUNK / 4), q4 = u % (RS_CHUNK / 4);
-            if (q4 < w4)
-                *(float4 *)(xs + RS_CHUNK * t + 4 * q4) = combine_x<PXBF16>(a, t, cb + 4 * q4, rpos + t * k, rgate + t * k);
+            if (q4 < w4) *(float4 *)(xs + RS_CHUNK * t + 4 * q4) = combine_x<PXBF16>(a, t, cb + 4 * q4);
         }
         __syncthreads();
 #pragma unroll
@@ -298,9 +285,9 @@ __global__ __launch_bounds__(512) void route_combine_small_kernel(LayerArgs a) {
             }
         }
     } else {
-        const int t = t0;
+        const int t = (int)blockIdx.x - nr * ng;
         for (int u = th; u < d / 4; u += blockDim.x) {
-            const float4 v = combine_x<PXBF16>(a, t, 4 * u, rpos, rgate);
+            const float4 v = combine_x<PXBF16>(a, t, 4 * u);
             *(float4 *)(xs + 4 * u) = v;
             *(float4 *)(a.x_cur + (size_t)t * d + 4 * u) = v;
         }
@@ -661,8 +648,8 @@ int route_logit_planes(int d) { return (d + RS_CHUNK - 1) / RS_CHUNK; }
 
 hipError_t launch_route_combine_small(const LayerArgs &a, hipStream_t s) {
     const int nr = route_logit_planes(a.d), ng = (a.E + RC_ROWS - 1) / RC_ROWS;
-    const size_t lds = sizeof(float) * (RC_ROUTE_WORDS + std::max((size_t)a.T * RS_CHUNK, (size_t)a.d + 4));
-    if (lds > LDS_LIMIT || a.T > CHUNK_TOK || a.k > 32 || !a.px || !a.x_cur || a.zplanes != nr)
+    const size_t lds = sizeof(float) * std::max((size_t)a.T * RS_CHUNK, (size_t)a.d + 4);
+    if (lds > LDS_LIMIT || a.T > CHUNK_TOK || a.k > 32 || !a.px || !a.x_cur || a.zplanes != nr || !a.ytok)
         return hipErrorInvalidValue;
     if (a.px_is_bf16)
         STRATA_LAUNCH(route_combine_small_kernel<1>, dim3(nr * ng + a.T), dim3(512), lds, s, a);

@@ -485,6 +485,11 @@ __device__ __forceinline__ void small_route_write(const LayerArgs &a, const Smal
         a.miss_w[mp] = L.sgate[th];
     }
     if (th == 0 && a.miss_count) *a.miss_count = mt;
+    if (a.mask && th < T) {
+        uint32_t b = 0;
+        for (int r = 0; r < k; ++r) b |= is_resident(a.mask, L.sidx[th * k + r]) ? 1u << r : 0u;
+        a.rbits[th] = (int32_t)b;
+    }
 }
 
 }  // namespace strata
