@@ -313,15 +313,19 @@ def _mask_words(E, resident):
 
 @pytest.mark.parametrize("E,k,d,f,bits,T,masked", [(16, 2, 384, 128, 3, 2, True), (64, 4, 1024, 256, 2, 8, True),
                                                     (1024, 8, 2048, 256, 3, 5, False),
-                                                    (512, 10, 2048, 768, 3, 3, True)])
+                                                    (512, 10, 2048, 768, 3, 3, True),
+                                                    (1000, 32, 256, 128, 3, 4, True),
+                                                    (32, 4, 128, 128, 2, 6, True)])
 def test_stack_equals_chained_layer_calls(E, k, d, f, bits, T, masked):
     """T = 2..8: in a stack each layer's combine runs inside the next layer's
     router kernel, which forms the logits as one partial sum per 256-column
     chunk.  Three layers in one call equal three chained one-layer calls bit
     for bit (output, residual, routing, miss lists), with resident masks
-    that differ per layer, d = 384 (two chunks, the second a half), 1024
-    and 2048, 8 tokens and E > 512; every layer's routing against the
-    oracle's chain, the last output and residual within the bound."""
+    that differ per layer, d = 128 (one half chunk), 384 (two chunks, the
+    second a half), 1024 and 2048, 8 tokens, E > 512, E = 1000 (not a
+    multiple of the 64 router rows per block) with k = 32; every layer's
+    routing against the oracle's chain, the last output and residual within
+    the bound."""
     w = synth.Workload(f"fold_E{E}_d{d}_b{bits}", E, k, d, f, bits, T, seed=0x5EED0C00 + E + d + T)
     rng = np.random.default_rng(0xF01D + E + d)
     Ls, refs, x0, xl = [], [], None, None
