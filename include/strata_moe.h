@@ -166,7 +166,12 @@ strata_status strata_moe_route(const strata_moe_shape *shape, const strata_moe_l
  *              NULL only when no layer has a resident mask; miss_cap = T*k never overflows.
  *   events     [host] array of 2*n_events hipEvent_t (as void*) or NULL: when given, the
  *              library records events[2i] before and events[2i+1] after the i-th kernel
- *              it enqueues (i < n_events), for per-kernel timing by the caller.
+ *              group it enqueues (i < n_events; strata_moe_kernel_names lists the groups of
+ *              a call), for per-kernel timing by the caller.
+ * The results do not depend on how the layers are split into calls: L layers in
+ * one call give the bits of L one-layer calls chained through resid_out (with
+ * STRATA_NORM_FIRST from the second on), although a T = 2..8 stack runs each
+ * layer's combine inside the next layer's router kernel.
  * T = 0 is a no-op returning STRATA_OK. */
 strata_status strata_moe_forward(const strata_moe_shape *shape, const strata_moe_layer *layers, int32_t L,
                                  const void *x, strata_xdtype xdtype, int32_t T, uint32_t flags, float *y_last,
