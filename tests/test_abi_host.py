@@ -163,3 +163,21 @@ def test_kernel_names_by_path():
     sh = brx.shape(512, 10, 2048, 768, 3)
     assert brx.kernel_names(sh, 1)[0] == "route_logits"
     assert "route_permute" in brx.kernel_names(sh, 4096)
+
+
+def test_kernel_names_list_every_group_of_a_call():
+    """One name per event pair a forward call records, in launch order: three
+    groups per layer at T = 1, four at T = 2..8 for one layer and 3L + 1 for
+    a stack (each layer's combine runs in the next layer's router kernel),
+    seven per layer on the matrix-core path; nothing for T < 1 or L < 1."""
+    sh = brx.shape(512, 10, 2048, 768, 3)
+    assert brx.kernel_names(sh, 1, 2) == ["route_logits", "route_gemv_gateup", "gemv_down_combine"] * 2
+    assert brx.kernel_names(sh, 5, 1) == ["route_logits", "route_gemv_gateup", "gemv_down", "combine"]
+    three = brx.kernel_names(sh, 5, 3)
+    assert three == (["route_logits", "route_gemv_gateup", "gemv_down"]
+                     + ["combine_route_logits", "route_gemv_gateup", "gemv_down"] * 2 + ["combine"])
+    assert len(brx.kernel_names(sh, 5, 48)) == 3 * 48 + 1
+    assert len(brx.kernel_names(sh, 4096, 2)) == 14
+    lib = brx.load_library()
+    assert lib.strata_moe_kernel_names(ctypes.byref(sh), 0, 1, None, 0) == 0
+    assert lib.strata_moe_kernel_names(ctypes.byref(sh), 5, 0, None, 0) == 0
