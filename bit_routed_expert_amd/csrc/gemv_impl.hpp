@@ -443,7 +443,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
     const SmallRoute L(lds + route_off, a.E);
     const int S = 64 / R, upl = (a.d / 32) / S;
     if (blockIdx.x == gridDim.x - 1) {
-        small_route_compute(a, L, a.z, a.inv_rms);
+        small_route_compute<true>(a, L, a.z, a.inv_rms);
         small_route_write(a, L);
         return;
     }
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_multi_kernel(LayerArgs a, int
         const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;
         qv[u] = q < nq ? (i < g.units ? a.xsum[(size_t)j * g.units + i] : __float_as_int(a.xscl[(size_t)j * g.G + i - g.units])) : 0;
     }
-    small_route_compute(a, L, a.z, a.inv_rms);
+    small_route_compute<true>(a, L, a.z, a.inv_rms);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int q = threadIdx.x + blockDim.x * u, j = q / per, i = q % per;

@@ -66,7 +66,15 @@ constexpr int TOPK_LDS_WORDS = 2 * TOPK_CAND;
 // the wave maximum of those values, then the smallest index among the lanes
 // holding it; the owning lane clears that key.  Lane r < k ends with pick r
 // in (*my_e, *my_k).  Keys are nonzero except for empty places.
-template <int JM>
+// Expert held in place j of a lane: lane + 64j (strided), or with CONTIG
+// 4*lane + (j mod 4) + 256*(j / 4), so a lane's places are four runs of 4
+// consecutive experts (16-byte loads).  Either way the places of one lane
+// rise with j, so "place ascending" inside a lane is "index ascending".
+template <bool CONTIG> __device__ __forceinline__ int topk_place(int lane, int j) {
+    return CONTIG ? 4 * lane + (j & 3) + 256 * (j >> 2) : lane + 64 * j;
+}
+
+template <int JM, bool CONTIG = false>
 __device__ __forceinline__ void topk_rounds(uint32_t (&kv)[JM], int k, int *my_e, uint32_t *my_k) {
     const int lane = threadIdx.x & 63;
     for (int r = 0; r < k; ++r) {
@@ -78,12 +86,12 @@ __device__ __forceinline__ void topk_rounds(uint32_t (&kv)[JM], int k, int *my_e
             bk = kv[j] > bk ? kv[j] : bk;
         }
         const uint32_t m = wave_allmax_u32(bk);
-        const uint32_t e = wave_allmin_u32(bk == m ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu);
+        const uint32_t e = wave_allmin_u32(bk == m ? (uint32_t)topk_place<CONTIG>(lane, bj) : 0xFFFFFFFFu);
         if (lane == r) {
             *my_e = (int)e;
             *my_k = m;
         }
-        if (bk == m && (uint32_t)(lane + 64 * bj) == e) {   // the owner clears its key
+        if (bk == m && (uint32_t)topk_place<CONTIG>(lane, bj) == e) {   // the owner clears its key
 #pragma unroll
             for (int j = 0; j < JM; ++j)
                 if (j == bj) kv[j] = 0u;
@@ -117,14 +125,52 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 //      every lane shares); rank r < k is pick r.
 // More than TOPK_CAND candidates (many equal values) take the rounds above.
 // planes > 1: z[e] is 0 + z[e] + z[pstride + e] + ... (planes terms, in
-// order), the loads of up to 64 values per lane issued before their adds.
-template <int JM>
+// order), the loads of up to 64 values per lane issued before their adds
+// (16-byte loads with CONTIG, which needs E a multiple of 4).
+template <int JM, bool CONTIG = false>
 __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int k, float scale, const float *bias,
                                                      uint32_t *cand, int *e_out, float *z_out, int planes = 1,
                                                      int pstride = 0) {
     const int lane = threadIdx.x & 63;
     float zv[JM], bv[JM];
-    if (planes == 1) {
+    if (CONTIG) {
+        // places 4q .. 4q+3 of this lane are experts 4*lane + 256q .. +3 (16 bytes, inside
+        // [0, E) or clamped into it; experts >= E are empty places below)
+#pragma unroll
+        for (int j = 0; j < JM; ++j) zv[j] = 0.f;
+        // one buffer resource over the planes (base and size in scalar registers), each load
+        // the lane's byte offset plus the plane's offset in a scalar register
+        const uint64_t zb = (uint64_t)z;
+        const uint32_t zlo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)zb);
+        const uint32_t zhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(zb >> 32));
+        const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(((uint64_t)zhi << 32) | zlo), 0, (int)(4u * (uint32_t)((planes - 1) * pstride + E)), 0x00020000);
+        const uint32_t pbytes = (uint32_t)__builtin_amdgcn_readfirstlane(4 * pstride);
+        uint32_t off4[JM / 4];
+#pragma unroll
+        for (int q = 0; q < JM / 4; ++q) off4[q] = 4u * (uint32_t)min(4 * lane + 256 * q, E - 4);
+        for (int p0 = 0; p0 < planes; p0 += 64 / JM) {
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            u32x4v pv[64 / JM][JM / 4];
+#pragma unroll
+            for (int p = 0; p < 64 / JM; ++p) {
+                const uint32_t so = (uint32_t)min(p0 + p, planes - 1) * pbytes;
+#pragma unroll
+                for (int q = 0; q < JM / 4; ++q)
+                    pv[p][q] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(zr, off4[q], so, 0));
+            }
+#pragma unroll
+            for (int p = 0; p < 64 / JM; ++p)
+#pragma unroll
+                for (int q = 0; q < JM / 4; ++q)
+                    if (p0 + p < planes) {
+                        zv[4 * q] += __uint_as_float(pv[p][q][0]);
+                        zv[4 * q + 1] += __uint_as_float(pv[p][q][1]);
+                        zv[4 * q + 2] += __uint_as_float(pv[p][q][2]);
+                        zv[4 * q + 3] += __uint_as_float(pv[p][q][3]);
+                    }
+        }
+    } else if (planes == 1) {
 #pragma unroll
         for (int j = 0; j < JM; ++j) zv[j] = z[min(lane + 64 * j, E - 1)];
     } else {
@@ -161,7 +207,7 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
     for (int j = 0; j < JM; ++j) bv[j] = 0.f;
     if (bias) {
 #pragma unroll
-        for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+        for (int j = 0; j < JM; ++j) bv[j] = bias[min(topk_place<CONTIG>(lane, j), E - 1)];
     }
     uint32_t kv[JM];   // value key (0 = empty)
     // the lane's two largest keys in order (value desc, place asc) and their places
@@ -169,7 +215,7 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
     int jm = 0, js = 0;
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
-        const int e = lane + 64 * j;
+        const int e = topk_place<CONTIG>(lane, j);
         kv[j] = (e < E) ? f32_key(zv[j] * scale + bv[j]) : 0u;
         const bool top = kv[j] > mx, second = !top && kv[j] > sx;
         js = top ? jm : (second ? j : js);
@@ -196,9 +242,9 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
         const int incl = wave_incl_scan(cnt);
         C = __builtin_amdgcn_readlane(incl, 63);
         const int pos = incl - cnt;
-        if (cnt >= 1 && pos < TOPK_CAND) c64[pos] = ((uint64_t)mx << 32) | (uint32_t)~(uint32_t)(lane + 64 * jm);
+        if (cnt >= 1 && pos < TOPK_CAND) c64[pos] = ((uint64_t)mx << 32) | (uint32_t)~(uint32_t)topk_place<CONTIG>(lane, jm);
         if (cnt == 2 && pos + 1 < TOPK_CAND)
-            c64[pos + 1] = ((uint64_t)sx << 32) | (uint32_t)~(uint32_t)(lane + 64 * js);
+            c64[pos + 1] = ((uint64_t)sx << 32) | (uint32_t)~(uint32_t)topk_place<CONTIG>(lane, js);
     } else {
         const int incl = wave_incl_scan(cnt);
         C = __builtin_amdgcn_readlane(incl, 63);
@@ -206,7 +252,7 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
             if (kv[j] >= P) {
-                if (pos < TOPK_CAND) c64[pos] = ((uint64_t)kv[j] << 32) | (uint32_t)~(uint32_t)(lane + 64 * j);
+                if (pos < TOPK_CAND) c64[pos] = ((uint64_t)kv[j] << 32) | (uint32_t)~(uint32_t)topk_place<CONTIG>(lane, j);
                 ++pos;
             }
         }
@@ -247,13 +293,16 @@ __device__ __forceinline__ void wave_topk_picks_fast(const float *z, int E, int 
             my_e = (int)~(uint32_t)v;
         }
     } else {
-        topk_rounds<JM>(kv, k, &my_e, &my_k);
+        topk_rounds<JM, CONTIG>(kv, k, &my_e, &my_k);
     }
     *e_out = my_e;
     *z_out = __uint_as_float((my_k & 0x80000000u) ? (my_k & 0x7FFFFFFFu) : ~my_k);
 }
 
 // Ordered top-k and gates of one token by one wave; lanes r < k write pick r.
+// PLANES: z may be several planes (added in order); E a multiple of 4 up to
+// 512 then takes the 16-byte-load layout.  Without it z is one plane.
+template <bool PLANES = false>
 __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float scale, const float *bias,
                                           uint32_t *cand, int32_t *idx_out, float *gate_out, int32_t *idx_out2,
                                           float *gate_out2, int32_t *idx_lds, float *gate_lds, int planes = 1,
@@ -261,10 +310,14 @@ __device__ __forceinline__ void wave_topk(const float *z, int E, int k, float sc
     const int lane = threadIdx.x & 63;
     int e;
     float v;
-    if (E <= 512)
-        wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
-    else
-        wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
+    if (PLANES) {
+        if (E <= 512 && (E & 3) == 0) wave_topk_picks_fast<8, true>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
+        else if (E <= 512) wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
+        else wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v, planes, pstride);
+    } else {
+        if (E <= 512) wave_topk_picks_fast<8>(z, E, k, scale, bias, cand, &e, &v);
+        else wave_topk_picks_fast<16>(z, E, k, scale, bias, cand, &e, &v);
+    }
     const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
     const float p = (lane < k) ? expf(v - top) : 0.f;
     const float s = wave_allsum_f32(p);
@@ -329,6 +382,7 @@ struct SmallRoute {
 // SMALL_ROUTE_WAVES waves) from the unnormalised logits z[t][E] and the
 // tokens' inverse RMS inv[t] (both may sit in LDS), then per-expert token
 // masks and the bitmap of picked resident experts.
+template <bool PLANES = false>
 __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const SmallRoute &L, const float *z,
                                                     const float *inv) {
     const int th = threadIdx.x, wave = th >> 6, nw = blockDim.x >> 6;
@@ -336,8 +390,9 @@ __device__ __forceinline__ void small_route_compute(const LayerArgs &a, const Sm
     for (int i = th; i < E; i += blockDim.x) L.tokmask[i] = 0;
     if (th < 32) L.picked[th] = 0;
     for (int t = wave; t < T; t += nw)
-        wave_topk(z + t * E, E, k, inv[t], a.bias, L.cand + (wave % SMALL_ROUTE_WAVES) * TOPK_LDS_WORDS, nullptr,
-                  nullptr, nullptr, nullptr, L.sidx + t * k, L.sgate + t * k, a.zplanes, T * E);
+        wave_topk<PLANES>(z + t * E, E, k, inv[t], a.bias, L.cand + (wave % SMALL_ROUTE_WAVES) * TOPK_LDS_WORDS,
+                          nullptr, nullptr, nullptr, nullptr, L.sidx + t * k, L.sgate + t * k, PLANES ? a.zplanes : 1,
+                          T * E);
     __syncthreads();
     if (th < T * k) {
         const int e = L.sidx[th];
