@@ -32,9 +32,46 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
 
+// The value of a 32-bit v in lane (lane ^ O), O a power of two up to 32,
+// without the LDS crossbar: DPP inside 16-lane rows (quad permutes for 1
+// and 2, the two 4-lane banks swapped by masked row shifts for 4, a row
+// rotation by 8 for 8) and the gfx950 row / half swaps for 16 and 32.  The
+// same partner as __shfl_xor(v, O), so sums and maxima keep their bits.
+template <int O> __device__ __forceinline__ int lane_xor(int v) {
+    static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "lane_xor: O");
+    if constexpr (O == 1) {
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (O == 2) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (O == 4) {
+        const int up = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xA, false);   // row_shr:4 into banks 1, 3
+        return __builtin_amdgcn_update_dpp(up, v, 0x104, 0xF, 0x5, false);          // row_shl:4 into banks 0, 2
+    } else if constexpr (O == 8) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // [0]: even rows twice, [1]: odd
+        return (threadIdx.x & 16) ? (int)r[0] : (int)r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // [0]: low half twice, [1]: high
+        return (threadIdx.x & 32) ? (int)r[0] : (int)r[1];
+    }
+}
+template <int O> __device__ __forceinline__ float lane_xor(float v) {
+    return __builtin_bit_cast(float, lane_xor<O>(__builtin_bit_cast(int, v)));
+}
+
+// The value in lane + 4 (inside each 16-lane row; lanes 12..15 get 0).
+__device__ __forceinline__ float lane_down4(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false));
+}
+
 template <typename T> __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    v += lane_xor<32>(v);
+    v += lane_xor<16>(v);
+    v += lane_xor<8>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<1>(v);
     return v;
 }
 // Sum over the wave by DPP (no LDS round trips): row sums by quad permutes
@@ -52,8 +89,12 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    v = fmaxf(v, lane_xor<32>(v));
+    v = fmaxf(v, lane_xor<16>(v));
+    v = fmaxf(v, lane_xor<8>(v));
+    v = fmaxf(v, lane_xor<4>(v));
+    v = fmaxf(v, lane_xor<2>(v));
+    v = fmaxf(v, lane_xor<1>(v));
     return v;
 }
 

@@ -60,8 +60,10 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(LayerArgs a) {
             *(uint4 *)(a.xa + pos) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             if (a.xpasses == 2) *(uint4 *)(a.xa + TD + pos) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
+        s += lane_xor<1>(s);
+        s += lane_xor<2>(s);
+        s += lane_xor<4>(s);
+        s += lane_xor<8>(s);
         if (valid && (q & 15) == 0) a.sx[(int64_t)t * nsteps + (q >> 4)] = s;
     }
 }

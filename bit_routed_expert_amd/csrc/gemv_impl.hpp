@@ -197,9 +197,12 @@ __device__ __forceinline__ void utile_compute(const UTile<BITS, UPLM> &wt, int R
             }
         }
     }
-    for (int o = R; o < 64; o <<= 1) {
+    // sum over the 64/R slices of each row (lane ^ R, ^ 2R, ...)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) res[t] += __shfl_xor(res[t], o, WAVE);
+    for (int t = 0; t < NT; ++t) {
+        if (R <= 8) res[t] += lane_xor<8>(res[t]);
+        if (R <= 16) res[t] += lane_xor<16>(res[t]);
+        if (R <= 32) res[t] += lane_xor<32>(res[t]);
     }
 }
 
@@ -431,7 +434,8 @@ __device__ __forceinline__ void gateup_wave_job(const LayerArgs &a, const WorkIt
                                  g.G, XGROUP_UNITS, tpk, res);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const float gv = res[j], u = __shfl_down(res[j], half, WAVE);
+        // the up row's result sits half lanes above (lanes < half read it)
+        const float gv = res[j], u = half == 4 ? lane_down4(res[j]) : half == 8 ? lane_xor<8>(res[j]) : lane_xor<16>(res[j]);
         if (lane < half) a.hf[(size_t)(it.slot0 + j) * a.f + c0 + lane] = gv / (1.f + expf(-gv)) * u;
     }
 }
@@ -565,13 +569,13 @@ template <int NT> struct HStage {
             float mx = 0.f;
 #pragma unroll
             for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
-            mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+            mx = fmaxf(mx, lane_xor<1>(mx));
+            mx = fmaxf(mx, lane_xor<2>(mx));
             const int E = fixed_point_exponent<XPLANES>(mx);
             uint32_t word[XPLANES];
             int sx = chunk_digits(h, E, word);
-            sx += __shfl_xor(sx, 1, WAVE);
-            sx += __shfl_xor(sx, 2, WAVE);
+            sx += lane_xor<1>(sx);
+            sx += lane_xor<2>(sx);
             if (c < nch) {
                 const int j = c / cps, cc = c % cps, U = cc / 4, q = cc % 4;
                 uint32_t *dst = wdig + j * dstride + dig_off(U, ups);
@@ -757,13 +761,13 @@ __global__ __launch_bounds__(DN_THREADS) void gemv_down_multi_kernel(LayerArgs a
         float mx = 0.f;
 #pragma unroll
         for (int n = 0; n < 8; ++n) mx = fmaxf(mx, fabsf(h[n]));
-        mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+        mx = fmaxf(mx, lane_xor<1>(mx));
+        mx = fmaxf(mx, lane_xor<2>(mx));
         const int E = fixed_point_exponent<XPLANES>(mx);
         uint32_t word[XPLANES];
         int sx = chunk_digits(h, E, word);
-        sx += __shfl_xor(sx, 1, WAVE);
-        sx += __shfl_xor(sx, 2, WAVE);
+        sx += lane_xor<1>(sx);
+        sx += lane_xor<2>(sx);
         if (c < nch) {
             const int j = c / cps, U = (c % cps) / 4, qq = c % 4;
             uint32_t *dst = dig + j * dstride + dig_off(U, upl);

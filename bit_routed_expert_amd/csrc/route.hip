@@ -45,8 +45,11 @@ __device__ void prep_token_row(const LayerArgs &a, int t, float inv, Load ld) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) m = fmaxf(m, fabsf(u[n]));
         // group max over the 32 chunks of a 256-column group (32 consecutive lanes)
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+        m = fmaxf(m, lane_xor<16>(m));
+        m = fmaxf(m, lane_xor<8>(m));
+        m = fmaxf(m, lane_xor<4>(m));
+        m = fmaxf(m, lane_xor<2>(m));
+        m = fmaxf(m, lane_xor<1>(m));
         int E = fixed_point_exponent<XPLANES>(m);
         int X[8];
         int sx = 0;
@@ -58,8 +61,8 @@ __device__ void prep_token_row(const LayerArgs &a, int t, float inv, Load ld) {
         uint32_t word[XPLANES];
         digit_words(X, word);
         // digit sums per 32-column unit (4 consecutive chunks)
-        sx += __shfl_xor(sx, 1, WAVE);
-        sx += __shfl_xor(sx, 2, WAVE);
+        sx += lane_xor<1>(sx);
+        sx += lane_xor<2>(sx);
         if (valid) {
             int U = c / 4, i = c % 4;
             uint32_t *dst = a.xq + ((size_t)t * (d / 32) + U) * (XPLANES * 4);
