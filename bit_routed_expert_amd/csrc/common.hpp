@@ -175,6 +175,12 @@ __device__ float token_inv_rms(const Args &a, int t, float *red) {
     return row_inv_rms(a.d, a.normalize, red, (int)blockDim.x, [&](int i) { return x_value(a, t, i); });
 }
 
+// silu(g) * u = g / (1 + e^-g) * u with the hardware 2^x and reciprocal
+// (about 1 ulp each), the same expression in every expert kernel.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
+}
+
 // Combine step of one pick: s += g * y, component by component (fma).
 __device__ __forceinline__ void combine_acc(float4 &s, float g, const float4 &y) {
     s.x = fmaf(g, y.x, s.x);

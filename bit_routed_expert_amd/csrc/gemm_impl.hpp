@@ -385,8 +385,7 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
         for (int v = 0; v < 16; ++v) {
             const uint32_t ml = mi * 32 + 8 * (v >> 2) + (v & 3);   // tile row minus 4h
             const float g = acc.A0[mi][v], u = acc.A1[mi][v];
-            // silu(g) * u with the hardware 2^x and reciprocal (about 1 ulp each)
-            const float hv = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
+            const float hv = silu_mul(g, u);
             const uint16_t hi = f2bf(hv);
             const float hif = bf16_to_float(hi);
             const uint16_t lo = f2bf(hv - hif);

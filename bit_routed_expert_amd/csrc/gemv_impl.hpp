@@ -344,7 +344,7 @@ __device__ __forceinline__ void gateup_body(const LayerArgs &a, const WorkItem &
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const float gv = res[j], u = g.gu[j * G * R + wave * R + lane];
-            a.hf[(size_t)(it.slot0 + j) * f + row0 + lane] = gv / (1.f + expf(-gv)) * u;
+            a.hf[(size_t)(it.slot0 + j) * f + row0 + lane] = silu_mul(gv, u);
         }
     }
 }
@@ -436,7 +436,7 @@ __device__ __forceinline__ void gateup_wave_job(const LayerArgs &a, const WorkIt
     for (int j = 0; j < NT; ++j) {
         // the up row's result sits half lanes above (lanes < half read it)
         const float gv = res[j], u = half == 4 ? lane_down4(res[j]) : half == 8 ? lane_xor<8>(res[j]) : lane_xor<16>(res[j]);
-        if (lane < half) a.hf[(size_t)(it.slot0 + j) * a.f + c0 + lane] = gv / (1.f + expf(-gv)) * u;
+        if (lane < half) a.hf[(size_t)(it.slot0 + j) * a.f + c0 + lane] = silu_mul(gv, u);
     }
 }
 
