@@ -223,13 +223,25 @@ __device__ __forceinline__ void mfma_step(const uint8_t *__restrict__ rd, const 
 
 __device__ __forceinline__ uint32_t bf16_bits(float v) { return __float_as_uint(v) >> 16; }  // exact for bf16 values
 
+// -OFF * S as three bf16 pieces (hi + mid + lo carry fp32's 24 bits), packed
+// as the first K columns of an A fragment: {hi | mid << 16, lo}.
+template <int BITS> __device__ __forceinline__ uint2 offset_pieces(float S) {
+    const float t = -Dec<BITS>::OFF * S;
+    const uint32_t hi = f2bf(t);
+    const float t1 = t - __uint_as_float(hi << 16);
+    const uint32_t mid = f2bf(t1);
+    const uint32_t lo = f2bf(t1 - __uint_as_float(mid << 16));
+    return make_uint2(hi | (mid << 16), lo);
+}
+
 // Enter scale block cb with raw fp16 scales q0, q1 of the two slices.
 template <int BITS, int NMT>
-__device__ __forceinline__ void enter_block(Acc2<BITS, NMT> &acc, const float *__restrict__ lds_s, int cb,
+__device__ __forceinline__ void enter_block(Acc2<BITS, NMT> &acc, const uint2 *__restrict__ lds_s, int cb,
                                             uint16_t q0, uint16_t q1, int n, int h) {
     const float f0 = half_to_float(q0), f1 = half_to_float(q1);
     const bool z0 = f0 == 0.f, z1 = f1 == 0.f;
-    const float r0 = z0 ? 1.f : acc.s0 / f0, r1 = z1 ? 1.f : acc.s1 / f1;
+    // ratio of the previous scale to this one (hardware reciprocal, 1 ulp)
+    const float r0 = z0 ? 1.f : acc.s0 * __builtin_amdgcn_rcpf(f0), r1 = z1 ? 1.f : acc.s1 * __builtin_amdgcn_rcpf(f1);
     acc.s0 = z0 ? acc.s0 : f0;
     acc.s1 = z1 ? acc.s1 : f1;
     acc.m0 = z0 ? 0u : Dec<BITS>::MASK;
@@ -249,12 +261,8 @@ __device__ __forceinline__ void enter_block(Acc2<BITS, NMT> &acc, const float *_
             acc.A1[mi][v] *= r1;
         }
         // -OFF * S of row mi*32 + n as three bf16 pieces in K columns 0..2
-        const float t = -Dec<BITS>::OFF * lds_s[cb * GEMM_BM + mi * 32 + n];
-        const uint32_t hi = f2bf(t);
-        const float t1 = t - __uint_as_float(hi << 16);
-        const uint32_t mid = f2bf(t1);
-        const uint32_t lo = f2bf(t1 - __uint_as_float(mid << 16));
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{hi | (mid << 16), lo, 0u, 0u});
+        const uint2 pc = lds_s[cb * GEMM_BM + mi * 32 + n];
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{pc.x, pc.y, 0u, 0u});
         acc.A0[mi] = mfma(av, w0, acc.A0[mi]);
         acc.A1[mi] = mfma(av, w1, acc.A1[mi]);
     }
@@ -266,7 +274,7 @@ __device__ __forceinline__ void enter_block(Acc2<BITS, NMT> &acc, const float *_
 // at step 0; sc0p/sc1p + (row*in + c) / 256: their scales.
 template <int BITS, int PASSES, int NMT>
 __device__ __forceinline__ void k_loop(Acc2<BITS, NMT> &acc, uint8_t *__restrict__ buf0, uint8_t *__restrict__ buf1,
-                                       const float *__restrict__ lds_s, __amdgpu_buffer_rsrc_t ar,
+                                       const uint2 *__restrict__ lds_s, __amdgpu_buffer_rsrc_t ar,
                                        const uint32_t aoff[3], uint32_t pass_bytes, __amdgpu_buffer_rsrc_t cr0,
                                        uint32_t co0, __amdgpu_buffer_rsrc_t cr1, uint32_t co1,
                                        const uint16_t *sc0p, const uint16_t *sc1p, int64_t rin0, int64_t rin1,
@@ -337,7 +345,7 @@ __device__ __forceinline__ int tile_token(const LayerArgs &a, const WorkItem &it
 template <int BITS, int PASSES, int NMT>
 __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &it, int ft,
                                             uint8_t *__restrict__ buf0, uint8_t *__restrict__ buf1,
-                                            float *__restrict__ lds_s, const int *__restrict__ lds_tok) {
+                                            uint2 *__restrict__ lds_s, const int *__restrict__ lds_tok) {
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int d = a.d, f = a.f, T = a.T;
@@ -348,7 +356,7 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &a, const WorkItem &
     for (int i = th; i < nblk * GEMM_BM; i += 256) {
         const int cb = i / GEMM_BM, m = i - cb * GEMM_BM;
         const float *p = a.sx + (int64_t)lds_tok[m] * nsteps + cb * spb;
-        lds_s[i] = spb == 2 ? p[0] + p[1] : p[0];
+        lds_s[i] = offset_pieces<BITS>(spb == 2 ? p[0] + p[1] : p[0]);
     }
     uint32_t aoff[3];   // byte offsets into xa (< 2^31: checked by the launcher)
 #pragma unroll
@@ -409,7 +417,7 @@ template <int BITS, int PASSES>
 __global__ __launch_bounds__(256, PASSES == 1 ? 3 : 2) void gemm_gateup_kernel(LayerArgs a, int nft) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[PASSES * GEMM_BM * GROW];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[PASSES * GEMM_BM * GROW];
-    __shared__ float lds_s[GMAX_STEPS * GEMM_BM];   // [step][row]
+    __shared__ uint2 lds_s[GMAX_STEPS * GEMM_BM];   // [scale block][row]: -OFF * S as bf16 pieces
     __shared__ int lds_tok[GEMM_BM];
     int tile, ft;
     if (!pick_tile(nft, *a.n_items, tile, ft)) return;
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(256, PASSES == 1 ? 3 : 2) void gemm_gateup_kernel(L
 template <int BITS, int NMT>
 __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it, int ft,
                                           uint8_t *__restrict__ buf0, uint8_t *__restrict__ buf1,
-                                          float *__restrict__ lds_s) {
+                                          uint2 *__restrict__ lds_s) {
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int d = a.d, f = a.f, T = a.T;
@@ -442,7 +450,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, const WorkItem &it
         const float *p = a.hs + (it.slot0 + min(m, ntok - 1)) * (f / 32) + gpb * cb;
         float acc = 0.f;
         for (int q = 0; q < gpb; ++q) acc += p[q];
-        lds_s[i] = acc;
+        lds_s[i] = offset_pieces<BITS>(acc);
     }
     uint32_t aoff[3];   // byte offsets into ha (< 2^31: checked by the launcher)
 #pragma unroll
@@ -482,7 +490,7 @@ template <int BITS>
 __global__ __launch_bounds__(256, 3) void gemm_down_kernel(LayerArgs a, int nft) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[2 * GEMM_BM * GROW];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[2 * GEMM_BM * GROW];
-    extern __shared__ float lds_s[];   // [scale block of the f features][row]
+    extern __shared__ uint2 lds_s[];   // [scale block of the f features][row]: -OFF * S as bf16 pieces
     int tile, ft;
     if (!pick_tile(nft, *a.n_items, tile, ft)) return;
     const WorkItem it = a.items[tile];
@@ -504,7 +512,7 @@ template <int BITS, int PASSES> hipError_t gemm_gateup_launch(const LayerArgs &a
 template <int BITS> hipError_t gemm_down_launch(const LayerArgs &a, int max_items, hipStream_t s) {
     const int nft = (a.d + 255) / 256;
     const int64_t blocks = ((int64_t)nft * max_items + 7) / 8 * 8;
-    const size_t lds_s = sizeof(float) * GEMM_BM * (a.f / ((a.f & 255) ? 128 : 256));   // S per scale block and row
+    const size_t lds_s = sizeof(uint2) * GEMM_BM * (a.f / ((a.f & 255) ? 128 : 256));   // per scale block and row
     if (((int64_t)a.T * a.k + a.T) * a.f * 4 > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // buffer offsets into ha
     STRATA_LAUNCH((gemm_down_kernel<BITS>), dim3((unsigned)blocks), dim3(256), lds_s, s, a, nft);
     return hipGetLastError();
