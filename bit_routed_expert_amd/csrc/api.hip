@@ -549,7 +549,7 @@ strata_status device_scratch(void **out) {
         void *p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
         if (e != hipSuccess) return hip_status(e);
-        if (!p) return STRATA_EHIP;
+        if (!p) return hip_status(hipErrorInvalidSymbol);
         g_scratch_ptr[dev] = p;
     }
     *out = g_scratch_ptr[dev];
