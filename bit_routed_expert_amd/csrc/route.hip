@@ -318,12 +318,15 @@ __global__ __launch_bounds__(256) void route_small_finish_kernel(LayerArgs a) {
 // sums are added in order.  The columns are cut into zsplit equal ranges of
 // whole blocks (grid z), each written as its own partial plane of z, so the
 // grid has enough blocks to hide memory latency; the top-k kernel adds the
-// planes in order.  Block tile 128 tokens x 64 experts; wave w owns tokens
-// 32*w .. +32 against all 64 experts (two 32x32 MFMA tiles).
-constexpr int RT_T = 128, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
+// planes in order.  Block tile 256 tokens x 64 experts (8 waves, so each
+// staged and split Wr tile feeds 256 tokens); wave w owns tokens 32*w .. +32
+// against all 64 experts (two 32x32 MFMA tiles).
+constexpr int RT_T = 256, RT_E = 64, RT_K = 32, RT_RS = RT_K + 8;   // LDS row: 32 bf16 + 16 B pad
+constexpr int RT_THREADS = 2 * RT_T;                                 // two threads stage each x row
+constexpr int RT_WC = RT_K * RT_E / RT_THREADS;                      // Wr columns staged per thread (4)
 
 template <int PX>
-__global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel(LayerArgs a) {
+__global__ __launch_bounds__(RT_THREADS, PX == 1 ? 4 : 2) void route_logits_mfma_kernel(LayerArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[PX][RT_T * RT_RS];
     __shared__ __attribute__((aligned(16))) uint16_t ws[3][RT_E * RT_RS];
     const int th = threadIdx.x, lane = th & 63, wv = th >> 6;
@@ -340,14 +343,14 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
     const int t0 = by * RT_T, e0 = bx * RT_E;
     const int d = a.d, T = a.T, E = a.E;
     const int kspan = d / a.zsplit, kbeg = bz * kspan, kend = kbeg + kspan;
-    // staging: x rows th/2 (16 columns each), Wr rows th/4 (8 columns each)
+    // staging: x rows th/2 (16 columns each), Wr rows th/8 (4 columns each)
     const int xr = th >> 1, xc = (th & 1) * 16;
-    const int wr = th >> 2, wc = (th & 3) * 8;
+    const int wr = th / (RT_K / RT_WC), wc = (th % (RT_K / RT_WC)) * RT_WC;
     const int64_t xoff = (int64_t)min(t0 + xr, T - 1) * d + xc;
     const int64_t woff = (int64_t)min(e0 + wr, E - 1) * d + wc;
     const bool wvalid = e0 + wr < E;
     float xv[16];
-    float4 wf[2];   // 8 columns of this thread's Wr row (fp32)
+    float4 wf;      // 4 columns of this thread's Wr row (fp32)
     auto load = [&](int k0) __attribute__((always_inline)) {
         if (a.x_is_bf16) {
             const uint4 *p = (const uint4 *)((const uint16_t *)a.x + xoff + k0);
@@ -366,9 +369,7 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
                 xv[4 * j] = q.x; xv[4 * j + 1] = q.y; xv[4 * j + 2] = q.z; xv[4 * j + 3] = q.w;
             }
         }
-        const float4 *pw = (const float4 *)(a.Wr + woff + k0);
-        wf[0] = pw[0];
-        wf[1] = pw[1];
+        wf = *(const float4 *)(a.Wr + woff + k0);
     };
     f32x16_t P[2], acc[2];
 #pragma unroll
@@ -379,10 +380,10 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
     for (int k0 = kbeg; k0 < kend; k0 += RT_K) {
         __syncthreads();
         {   // pieces into LDS: Wr = hi + mid + lo exactly, two columns packed per word
-            const float w[8] = {wf[0].x, wf[0].y, wf[0].z, wf[0].w, wf[1].x, wf[1].y, wf[1].z, wf[1].w};
-            uint32_t u[3][4];
+            const float w[4] = {wf.x, wf.y, wf.z, wf.w};
+            uint32_t u[3][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 uint16_t a0, b0, c0, a1, b1, c1;
                 split3(w[2 * j], a0, b0, c0);
                 split3(w[2 * j + 1], a1, b1, c1);
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256, PX == 1 ? 4 : 2) void route_logits_mfma_kernel
                 u[2][j] = wvalid ? ((uint32_t)c0 | ((uint32_t)c1 << 16)) : 0u;
             }
 #pragma unroll
-            for (int q = 0; q < 3; ++q) *(uint4 *)(ws[q] + wr * RT_RS + wc) = make_uint4(u[q][0], u[q][1], u[q][2], u[q][3]);
+            for (int q = 0; q < 3; ++q) *(uint2 *)(ws[q] + wr * RT_RS + wc) = make_uint2(u[q][0], u[q][1]);
             uint16_t hx[PX][16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -679,9 +680,9 @@ hipError_t launch_route_logits(const LayerArgs &a, hipStream_t s) {
     const dim3 grid((a.E + RT_E - 1) / RT_E, (a.T + RT_T - 1) / RT_T, a.zsplit);
     if (a.d % RT_K || a.zsplit < 1 || a.d % a.zsplit || (a.d / a.zsplit) % RT_K || a.E > 1024) return hipErrorInvalidValue;
     if (a.x_is_bf16)
-        STRATA_LAUNCH(route_logits_mfma_kernel<1>, grid, dim3(256), 0, s, a);
+        STRATA_LAUNCH(route_logits_mfma_kernel<1>, grid, dim3(RT_THREADS), 0, s, a);
     else
-        STRATA_LAUNCH(route_logits_mfma_kernel<3>, grid, dim3(256), 0, s, a);
+        STRATA_LAUNCH(route_logits_mfma_kernel<3>, grid, dim3(RT_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
