@@ -181,10 +181,11 @@ def test_prepared_call_equals_forward(name, T):
             np.testing.assert_array_equal(resid.cpu().numpy(), ref[1])
 
 
-@pytest.mark.parametrize("T", [3, 12])
+@pytest.mark.parametrize("T", [3, 12, 300])
 def test_fp32_input_with_norm_first(T):
     """fp32 residual-stream input, RMS-normalised before routing: the decode
-    path (T = 3) and the matrix-core path with hi/lo bf16 activations (T = 12)."""
+    path (T = 3) and the matrix-core path with hi/lo bf16 activations (T = 12;
+    T = 300 spans two 256-token router tiles, the second partial)."""
     w = synth.WORKLOADS["decode"]
     L = W.layer_data(w, 0)
     rng = np.random.default_rng(11 + T)

@@ -156,6 +156,21 @@ def test_ragged_batches_full_size_layer(T):
     G.assert_close(got["y"], ref["out"])
 
 
+def test_full_size_layer_two_router_tiles():
+    """300 tokens: two 256-token tiles of the larger-T router (the second
+    partial) and 96-token expert tiles, against the grouped oracle."""
+    w = synth.WORKLOADS["decode"]
+    L = W.layer_data(w, 1)
+    T = 300
+    x, _ = W.draw_tokens(w, L["Wr"], None, range(T), rep=13)
+    u = synth.bf16_to_f32(x)
+    print(f"case full-size layer T={T}", flush=True)
+    ref = oracle.moe_layer(w.bits, w.n_experts, w.top_k, w.d_model, w.d_ff, u, L["Wr"], L["codes"], L["scales"])
+    got = G.run_forward(w, [G.layer_to_dev(L)], G.dev(x), 0, T)
+    G.assert_route_equal(got["route"][0], ref)
+    G.assert_close(got["y"], ref["out"])
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 8, 20])
 def test_small_layer_token_counts(T):
     w = synth.WORKLOADS["tiny"]
