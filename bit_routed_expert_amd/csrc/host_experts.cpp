@@ -39,16 +39,21 @@ typedef float vf __attribute__((vector_size(64)));      // 16 fp32 lanes
 typedef uint32_t vu __attribute__((vector_size(64)));
 typedef int32_t vi __attribute__((vector_size(64)));
 
-// Exact value of an IEEE binary16 bit pattern.
+// Exact value of an IEEE binary16 bit pattern: normal numbers by moving the
+// exponent and mantissa fields into place, subnormals as m * 2^-24 (exact).
 static inline float half_to_float(uint16_t h) {
-    const uint32_t s = (uint32_t)(h >> 15) << 31, e = (h >> 10) & 0x1F, m = h & 0x3FF;
-    float v;
-    if (e == 0) v = ldexpf((float)m, -24);
-    else if (e == 31) v = m ? NAN : INFINITY;
-    else v = ldexpf((float)(1024 + m), (int)e - 25);
+    const uint32_t s = (uint32_t)(h & 0x8000u) << 16, e = (h >> 10) & 0x1F, m = h & 0x3FF;
     uint32_t u;
-    memcpy(&u, &v, 4);
+    if (e == 0) {
+        const float v = (float)m * 0x1p-24f;
+        memcpy(&u, &v, 4);
+    } else if (e == 31) {
+        u = m ? 0x7FC00000u : 0x7F800000u;
+    } else {
+        u = ((e + 112) << 23) | (m << 13);
+    }
     u |= s;
+    float v;
     memcpy(&v, &u, 4);
     return v;
 }
@@ -115,18 +120,24 @@ static inline float hsum(vf v) {
     return a[0];
 }
 
+// 16 floats from any address, as one vector load (a single-vector copy; a
+// copy into an array of vectors went through the stack as 16-byte pieces and
+// stalled every reload of it).
+static inline vf ldv(const float *p) {
+    vf v;
+    __builtin_memcpy(&v, p, sizeof v);
+    return v;
+}
+
 // w . x over n (a multiple of 64) columns: four partial sums of 16 lanes
 // (columns i % 64 in [16q, 16q + 16) go to sum q), added in a fixed order.
 static inline float dot(const float *w, const float *x, int n) {
     vf a0 = {}, a1 = {}, a2 = {}, a3 = {};
     for (int i = 0; i < n; i += 64) {
-        vf p[4], b[4];
-        memcpy(p, w + i, 256);
-        memcpy(b, x + i, 256);
-        a0 += p[0] * b[0];
-        a1 += p[1] * b[1];
-        a2 += p[2] * b[2];
-        a3 += p[3] * b[3];
+        a0 += ldv(w + i) * ldv(x + i);
+        a1 += ldv(w + i + 16) * ldv(x + i + 16);
+        a2 += ldv(w + i + 32) * ldv(x + i + 32);
+        a3 += ldv(w + i + 48) * ldv(x + i + 48);
     }
     return hsum((a0 + a1) + (a2 + a3));
 }
@@ -136,22 +147,71 @@ static inline float dot(const float *w, const float *x, int n) {
 static inline void dot2(const float *w0, const float *w1, const float *x, int n, float &r0, float &r1) {
     vf a0 = {}, a1 = {}, a2 = {}, a3 = {}, c0 = {}, c1 = {}, c2 = {}, c3 = {};
     for (int i = 0; i < n; i += 64) {
-        vf p[4], q[4], b[4];
-        memcpy(p, w0 + i, 256);
-        memcpy(q, w1 + i, 256);
-        memcpy(b, x + i, 256);
-        a0 += p[0] * b[0];
-        a1 += p[1] * b[1];
-        a2 += p[2] * b[2];
-        a3 += p[3] * b[3];
-        c0 += q[0] * b[0];
-        c1 += q[1] * b[1];
-        c2 += q[2] * b[2];
-        c3 += q[3] * b[3];
+        const vf b0 = ldv(x + i), b1 = ldv(x + i + 16), b2 = ldv(x + i + 32), b3 = ldv(x + i + 48);
+        a0 += ldv(w0 + i) * b0;
+        a1 += ldv(w0 + i + 16) * b1;
+        a2 += ldv(w0 + i + 32) * b2;
+        a3 += ldv(w0 + i + 48) * b3;
+        c0 += ldv(w1 + i) * b0;
+        c1 += ldv(w1 + i + 16) * b1;
+        c2 += ldv(w1 + i + 32) * b2;
+        c3 += ldv(w1 + i + 48) * b3;
     }
     r0 = hsum((a0 + a1) + (a2 + a3));
     r1 = hsum((c0 + c1) + (c2 + c3));
 }
+
+// The gate and up rows against two vectors, each of the four dot products
+// summed exactly as dot() sums it (the row loads are shared).
+static inline void dot2x2(const float *w0, const float *w1, const float *x, const float *y, int n, float r[4]) {
+    vf a0 = {}, a1 = {}, a2 = {}, a3 = {}, c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    vf e0 = {}, e1 = {}, e2 = {}, e3 = {}, g0 = {}, g1 = {}, g2 = {}, g3 = {};
+    for (int i = 0; i < n; i += 64) {
+        const vf p0 = ldv(w0 + i), p1 = ldv(w0 + i + 16), p2 = ldv(w0 + i + 32), p3 = ldv(w0 + i + 48);
+        const vf q0 = ldv(w1 + i), q1 = ldv(w1 + i + 16), q2 = ldv(w1 + i + 32), q3 = ldv(w1 + i + 48);
+        const vf b0 = ldv(x + i), b1 = ldv(x + i + 16), b2 = ldv(x + i + 32), b3 = ldv(x + i + 48);
+        a0 += p0 * b0;
+        a1 += p1 * b1;
+        a2 += p2 * b2;
+        a3 += p3 * b3;
+        c0 += q0 * b0;
+        c1 += q1 * b1;
+        c2 += q2 * b2;
+        c3 += q3 * b3;
+        const vf d0 = ldv(y + i), d1 = ldv(y + i + 16), d2 = ldv(y + i + 32), d3 = ldv(y + i + 48);
+        e0 += p0 * d0;
+        e1 += p1 * d1;
+        e2 += p2 * d2;
+        e3 += p3 * d3;
+        g0 += q0 * d0;
+        g1 += q1 * d1;
+        g2 += q2 * d2;
+        g3 += q3 * d3;
+    }
+    r[0] = hsum((a0 + a1) + (a2 + a3));
+    r[1] = hsum((c0 + c1) + (c2 + c3));
+    r[2] = hsum((e0 + e1) + (e2 + e3));
+    r[3] = hsum((g0 + g1) + (g2 + g3));
+}
+
+// One row against four vectors, each summed exactly as dot() sums it.
+static inline void dotx4(const float *w, const float *const x[4], int n, float r[4]) {
+    vf a[4][4] = {};
+    for (int i = 0; i < n; i += 64) {
+        const vf p0 = ldv(w + i), p1 = ldv(w + i + 16), p2 = ldv(w + i + 32), p3 = ldv(w + i + 48);
+#pragma GCC unroll 4
+        for (int v = 0; v < 4; ++v) {
+            a[v][0] += p0 * ldv(x[v] + i);
+            a[v][1] += p1 * ldv(x[v] + i + 16);
+            a[v][2] += p2 * ldv(x[v] + i + 32);
+            a[v][3] += p3 * ldv(x[v] + i + 48);
+        }
+    }
+#pragma GCC unroll 4
+    for (int v = 0; v < 4; ++v) r[v] = hsum((a[v][0] + a[v][1]) + (a[v][2] + a[v][3]));
+}
+
+static inline float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
 // Phase A task: rows [j0, j1) of h for every miss of expert e.
 void gateup_rows(const HostMissArgs &a, int e, int j0, int j1) {
@@ -163,11 +223,19 @@ void gateup_rows(const HostMissArgs &a, int e, int j0, int j1) {
     for (int j = j0; j < j1; ++j) {
         decode_row(a.bits, cg, sg, d, j, wg);
         decode_row(a.bits, cu, su, d, j, wu);
-        for (int q = a.gstart[e]; q < a.gstart[e + 1]; ++q) {
+        int q = a.gstart[e];
+        for (; q + 2 <= a.gstart[e + 1]; q += 2) {   // two misses per pass over the rows
+            const int m0 = a.order[q], m1 = a.order[q + 1];
+            float r[4];
+            dot2x2(wg, wu, a.u + (int64_t)a.miss_te[2 * m0] * d, a.u + (int64_t)a.miss_te[2 * m1] * d, d, r);
+            a.h[(int64_t)m0 * f + j] = silu_mul(r[0], r[1]);
+            a.h[(int64_t)m1 * f + j] = silu_mul(r[2], r[3]);
+        }
+        for (; q < a.gstart[e + 1]; ++q) {
             const int m = a.order[q], t = a.miss_te[2 * m];
             float g, u;
             dot2(wg, wu, a.u + (int64_t)t * d, d, g, u);
-            a.h[(int64_t)m * f + j] = g / (1.f + expf(-g)) * u;
+            a.h[(int64_t)m * f + j] = silu_mul(g, u);
         }
     }
 }
@@ -186,7 +254,18 @@ void down_cols(const HostMissArgs &a, const int32_t *experts, int ne, int i0, in
         const uint16_t *sd = a.scales + (int64_t)e * 3 * mat_blocks + 2 * mat_blocks;
         for (int i = i0; i < i1; ++i) {
             decode_row(a.bits, cd, sd, f, i, wd);
-            for (int q = a.gstart[e]; q < a.gstart[e + 1]; ++q) {
+            int q = a.gstart[e];
+            for (; q + 4 <= a.gstart[e + 1]; q += 4) {   // four misses per pass over the row, added in list order
+                const float *hx[4];
+                for (int v = 0; v < 4; ++v) hx[v] = a.h + (int64_t)a.order[q + v] * f;
+                float r[4];
+                dotx4(wd, hx, f, r);
+                for (int v = 0; v < 4; ++v) {
+                    const int m = a.order[q + v];
+                    a.y_add[(int64_t)a.miss_te[2 * m] * d + i] += a.miss_w[m] * r[v];
+                }
+            }
+            for (; q < a.gstart[e + 1]; ++q) {
                 const int m = a.order[q], t = a.miss_te[2 * m];
                 a.y_add[(int64_t)t * d + i] += a.miss_w[m] * dot(wd, a.h + (int64_t)m * f, f);
             }
