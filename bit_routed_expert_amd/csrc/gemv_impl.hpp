@@ -606,6 +606,8 @@ __host__ __device__ inline int down_one_lds_words(int k, int f, int R) {
     return (k + 1) * R + (k + 1) * (units * XPLANES * 4 + S * 4 + 2 * units) + 3 * k;
 }
 
+constexpr int DN1_MAX_WAVES = 12;   // one wave per pick plus the shared expert's (k + 1 <= 12)
+
 template <int BITS, int UPLM>
 __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, int R) {
     extern __shared__ uint32_t lds[];
@@ -625,6 +627,13 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
     int slot = wave < k ? wave : k;
     HStage<1> st;
     if (fast) st.load(a, slot);
+    // residual input of this block's rows (threads th < R, R < blockDim.x),
+    // loaded now so that the final combine waits for no memory round trip
+    float xin = 0.f;
+    if (a.x_next && th < R) {
+        const size_t o = (size_t)row0 + th;
+        xin = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
+    }
     int pe = 0, pp = 0;
     float pg = 0.f;
     if (wave == 0 && lane < k) {
@@ -656,16 +665,26 @@ __global__ __launch_bounds__(768) void gemv_down_rows_one_kernel(LayerArgs a, in
         con[lane] = is_resident(a.mask, pe) ? 1 : 0;
     }
     __syncthreads();
-    for (int i = th; i < R; i += blockDim.x) {
+    if (th < R) {   // row i = th: shared expert, then the picks in order (every LDS read issued before the sums)
+        const int i = th;
+        int sl[DN1_MAX_WAVES];
+        float gv[DN1_MAX_WAVES], yv[DN1_MAX_WAVES];
+        bool on[DN1_MAX_WAVES];
+#pragma unroll
+        for (int r = 0; r < DN1_MAX_WAVES; ++r) {
+            sl[r] = r < k ? cp[r] : k;
+            gv[r] = r < k ? cg[r] : 0.f;
+            on[r] = r < k && con[r] != 0;
+        }
+#pragma unroll
+        for (int r = 0; r < DN1_MAX_WAVES; ++r) yv[r] = ybuf[sl[r] * R + i];
         float s = ybuf[k * R + i];
-        for (int r = 0; r < k; ++r)
-            if (con[r]) s = fmaf(cg[r], ybuf[cp[r] * R + i], s);
+#pragma unroll
+        for (int r = 0; r < DN1_MAX_WAVES; ++r)
+            if (on[r]) s = fmaf(gv[r], yv[r], s);
         const size_t o = (size_t)row0 + i;
         a.out[o] = s;
-        if (a.x_next) {
-            const float xv = a.x_is_bf16 ? bf16_to_float(((const uint16_t *)a.x)[o]) : ((const float *)a.x)[o];
-            a.x_next[o] = xv + s;
-        }
+        if (a.x_next) a.x_next[o] = xin + s;
     }
 }
 
@@ -849,7 +868,7 @@ template <int BITS> hipError_t down_multi_launch(const LayerArgs &a, int max_ite
 template <int BITS> hipError_t down_one_launch(const LayerArgs &a, hipStream_t s) {
     const int R = 64 / unit_slices(a.f, 8);
     const size_t lds = 4 * (size_t)down_one_lds_words(a.k, a.f, R);
-    if (a.T != 1 || lds > LDS_LIMIT || a.k + 1 > 12) return hipErrorInvalidValue;
+    if (a.T != 1 || lds > LDS_LIMIT || a.k + 1 > DN1_MAX_WAVES) return hipErrorInvalidValue;
     const int upl = (a.f / 32) / (64 / R);
     const dim3 grid(a.d / R), block(64 * (a.k + 1));
     if (upl == 3)   // d_ff = 768
