@@ -20,6 +20,16 @@ constexpr int CB_COLS = 1024;   // columns per block (4 per thread)
 // Y rows in token order (pick r of token t at row t*k + r) and residency
 // from rbits, so the rows load with the gates in one round trip; else the
 // rows sit at the picks' slots (pos) and residency comes from the mask.
+// Four consecutive values of the residual input x (bf16 or fp32) as fp32.
+template <int XBF16> __device__ __forceinline__ float4 load_x4(const void *x, int64_t at) {
+    if (XBF16) {
+        const uint2 q = *(const uint2 *)((const uint16_t *)x + at);
+        return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
+                           __uint_as_float(q.y & 0xFFFF0000u));
+    }
+    return *(const float4 *)((const float *)x + at);
+}
+
 template <int XBF16, int YTOK>
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     const int d = a.d, k = a.k, T = a.T;
@@ -30,6 +40,8 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
     const float *__restrict__ Y = a.Y;
     const int64_t row = (int64_t)t * d + i;
     float4 s = *(const float4 *)(Y + ((int64_t)T * k + t) * d + i);
+    // the residual input, loaded with the first reads (not after the output store)
+    const float4 xv = a.x_next ? load_x4<XBF16>(a.x, row) : make_float4(0.f, 0.f, 0.f, 0.f);
     const uint32_t rb = (YTOK && a.mask) ? (uint32_t)a.rbits[t] : 0xFFFFFFFFu;
     for (int r0 = 0; r0 < k; r0 += KB) {
         int pr[KB];
@@ -44,11 +56,12 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
                         pr[r] = t * k + r0 + r;
                         gr[r] = a.gate[t * k + r0 + r];
                     }
-                } else {
-                    const int e = a.idx[t * k + r0 + r];
+                } else {   // pick, slot and gate read together; the mask test picks them afterwards
+                    const int e = a.idx[t * k + r0 + r], p = a.pos[t * k + r0 + r];
+                    const float g = a.gate[t * k + r0 + r];
                     if (!a.mask || ((a.mask[e >> 5] >> (e & 31)) & 1u)) {
-                        pr[r] = a.pos[t * k + r0 + r];
-                        gr[r] = a.gate[t * k + r0 + r];
+                        pr[r] = p;
+                        gr[r] = g;
                     }
                 }
             }
@@ -68,17 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
         }
     }
     *(float4 *)(a.out + row) = s;
-    if (a.x_next) {
-        float4 xv;
-        if (XBF16) {
-            const uint2 q = *(const uint2 *)((const uint16_t *)a.x + row);
-            xv = make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
-                             __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
-        } else {
-            xv = *(const float4 *)((const float *)a.x + row);
-        }
-        *(float4 *)(a.x_next + row) = make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w);
-    }
+    if (a.x_next) *(float4 *)(a.x_next + row) = make_float4(xv.x + s.x, xv.y + s.y, xv.z + s.z, xv.w + s.w);
 }
 
 // out[i] += add[i], then x_next[i] = x[i] + out[i] (4 values per thread).
@@ -88,19 +91,10 @@ __global__ __launch_bounds__(256) void add_rows_kernel(LayerArgs a, const float 
     if (i >= (int64_t)a.T * a.d) return;
     const float4 v = *(const float4 *)(add + i);
     float4 o = *(const float4 *)(a.out + i);
+    const float4 xv = a.x_next ? load_x4<XBF16>(a.x, i) : make_float4(0.f, 0.f, 0.f, 0.f);
     o = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
     *(float4 *)(a.out + i) = o;
-    if (a.x_next) {
-        float4 xv;
-        if (XBF16) {
-            const uint2 q = *(const uint2 *)((const uint16_t *)a.x + i);
-            xv = make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
-                             __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
-        } else {
-            xv = *(const float4 *)((const float *)a.x + i);
-        }
-        *(float4 *)(a.x_next + i) = make_float4(xv.x + o.x, xv.y + o.y, xv.z + o.z, xv.w + o.w);
-    }
+    if (a.x_next) *(float4 *)(a.x_next + i) = make_float4(xv.x + o.x, xv.y + o.y, xv.z + o.z, xv.w + o.w);
 }
 
 hipError_t launch_add_rows(const LayerArgs &a, const float *add, hipStream_t s) {
