@@ -476,7 +476,7 @@ def _coprocess_timing(res, sh, ws, ws_bytes, dev, step_layer):
     macs = n * 3 * d * w.d_ff
     return {"ms_per_prompt": round(times[-1] * 1e3, 2), "tokens_per_s": round(T * calls / times[-1], 1),
             "host_misses_ms_per_chunk": round(host_s * 1e3, 2), "misses_chunk0": n,
-            "host_gflops": round(2 * macs / host_s / 1e9, 1), "host_isa": brx.host_isa(), "host_threads": threads,
+            "host_gflops": round(2 * macs / host_s / 1e9, 1), "host_isa": brx.host_isa(), "host_threads": threads, "cpu_topology": _cpu_topology(),
             "what": "each chunk: GPU routing and resident experts, miss list and input copied to the host on a "
                     "second stream, host FFNs of the misses from host-resident packed weights, merged on the GPU"}
 
@@ -789,6 +789,24 @@ def _cpu_model():
     return platform.processor() or "unknown"
 
 
+def _cpu_topology():
+    """Sockets, cores per socket and threads per core as lscpu reports them."""
+    keys = {"Socket(s):": "sockets", "Core(s) per socket:": "cores_per_socket", "Thread(s) per core:": "threads_per_core"}
+    topo = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            for k, name in keys.items():
+                if line.startswith(k):
+                    try:
+                        topo[name] = int(line.split(":", 1)[1].strip())
+                    except ValueError:
+                        pass
+    except Exception:
+        pass
+    return topo
+
+
 def _cpu_baseline(name, w, target_s, bias=None, mask=None):
     """The oracle (grouped evaluation: each needed expert dequantised once,
     then its tokens) on a bounded sample of the workload, with every thread
@@ -818,7 +836,7 @@ def _cpu_baseline(name, w, target_s, bias=None, mask=None):
 
     tc = w.tokens_per_call
     rec = {"unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": _cpu_model(),
-           "host_cpus_visible": os.cpu_count()}
+           "cpu_topology": _cpu_topology(), "host_cpus_visible": os.cpu_count()}
     if tc <= 8:
         n, el = run(tc, 64, cores, target_s)
         rec["value"] = round(n * tc / el / w.layers, 4)
