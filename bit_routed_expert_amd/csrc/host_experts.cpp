@@ -13,7 +13,7 @@
 // be shared with the other at link time; the caller picks one set at run
 // time and runs the tasks on its threads.  Arithmetic is fp32 with fused
 // multiply-adds: weights scale * (code - c0) are exact in fp32; every dot
-// product keeps four 16-lane partial sums and adds them in a fixed tree,
+// product keeps two 16-lane partial sums and adds them in a fixed tree,
 // so results do not depend on the thread count.
 //
 // Two phases:
@@ -129,86 +129,54 @@ static inline vf ldv(const float *p) {
     return v;
 }
 
-// w . x over n (a multiple of 64) columns: four partial sums of 16 lanes
-// (columns i % 64 in [16q, 16q + 16) go to sum q), added in a fixed order.
-static inline float dot(const float *w, const float *x, int n) {
-    vf a0 = {}, a1 = {}, a2 = {}, a3 = {};
-    for (int i = 0; i < n; i += 64) {
-        a0 += ldv(w + i) * ldv(x + i);
-        a1 += ldv(w + i + 16) * ldv(x + i + 16);
-        a2 += ldv(w + i + 32) * ldv(x + i + 32);
-        a3 += ldv(w + i + 48) * ldv(x + i + 48);
-    }
-    return hsum((a0 + a1) + (a2 + a3));
-}
-
-// Two rows against one vector (the gate and up rows of one h column), each
-// summed exactly as dot() sums it.
-static inline void dot2(const float *w0, const float *w1, const float *x, int n, float &r0, float &r1) {
-    vf a0 = {}, a1 = {}, a2 = {}, a3 = {}, c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    for (int i = 0; i < n; i += 64) {
-        const vf b0 = ldv(x + i), b1 = ldv(x + i + 16), b2 = ldv(x + i + 32), b3 = ldv(x + i + 48);
-        a0 += ldv(w0 + i) * b0;
-        a1 += ldv(w0 + i + 16) * b1;
-        a2 += ldv(w0 + i + 32) * b2;
-        a3 += ldv(w0 + i + 48) * b3;
-        c0 += ldv(w1 + i) * b0;
-        c1 += ldv(w1 + i + 16) * b1;
-        c2 += ldv(w1 + i + 32) * b2;
-        c3 += ldv(w1 + i + 48) * b3;
-    }
-    r0 = hsum((a0 + a1) + (a2 + a3));
-    r1 = hsum((c0 + c1) + (c2 + c3));
-}
-
-// The gate and up rows against two vectors, each of the four dot products
-// summed exactly as dot() sums it (the row loads are shared).
-static inline void dot2x2(const float *w0, const float *w1, const float *x, const float *y, int n, float r[4]) {
-    vf a0 = {}, a1 = {}, a2 = {}, a3 = {}, c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    vf e0 = {}, e1 = {}, e2 = {}, e3 = {}, g0 = {}, g1 = {}, g2 = {}, g3 = {};
-    for (int i = 0; i < n; i += 64) {
-        const vf p0 = ldv(w0 + i), p1 = ldv(w0 + i + 16), p2 = ldv(w0 + i + 32), p3 = ldv(w0 + i + 48);
-        const vf q0 = ldv(w1 + i), q1 = ldv(w1 + i + 16), q2 = ldv(w1 + i + 32), q3 = ldv(w1 + i + 48);
-        const vf b0 = ldv(x + i), b1 = ldv(x + i + 16), b2 = ldv(x + i + 32), b3 = ldv(x + i + 48);
-        a0 += p0 * b0;
-        a1 += p1 * b1;
-        a2 += p2 * b2;
-        a3 += p3 * b3;
-        c0 += q0 * b0;
-        c1 += q1 * b1;
-        c2 += q2 * b2;
-        c3 += q3 * b3;
-        const vf d0 = ldv(y + i), d1 = ldv(y + i + 16), d2 = ldv(y + i + 32), d3 = ldv(y + i + 48);
-        e0 += p0 * d0;
-        e1 += p1 * d1;
-        e2 += p2 * d2;
-        e3 += p3 * d3;
-        g0 += q0 * d0;
-        g1 += q1 * d1;
-        g2 += q2 * d2;
-        g3 += q3 * d3;
-    }
-    r[0] = hsum((a0 + a1) + (a2 + a3));
-    r[1] = hsum((c0 + c1) + (c2 + c3));
-    r[2] = hsum((e0 + e1) + (e2 + e3));
-    r[3] = hsum((g0 + g1) + (g2 + g3));
-}
-
-// One row against four vectors, each summed exactly as dot() sums it.
-static inline void dotx4(const float *w, const float *const x[4], int n, float r[4]) {
-    vf a[4][4] = {};
-    for (int i = 0; i < n; i += 64) {
-        const vf p0 = ldv(w + i), p1 = ldv(w + i + 16), p2 = ldv(w + i + 32), p3 = ldv(w + i + 48);
+// Rows w0 and w1 against NV vectors x[v] over n (a multiple of 32) columns.
+// Every dot product keeps two partial sums of 16 lanes (columns i % 32 in
+// [16p, 16p + 16) go to sum p) and ends with hsum(sum0 + sum1), whatever NV
+// is, so a result does not depend on how the vectors were grouped; the row
+// loads are shared by the NV vectors (0.75 loads per multiply-add at NV = 4).
+// r[2v] = w0 . x[v], r[2v + 1] = w1 . x[v].
+template <int NV> static inline void dots2(const float *w0, const float *w1, const float *const *x, int n, float *r) {
+    vf a[NV][4];   // [vector][row 0 sum 0, row 0 sum 1, row 1 sum 0, row 1 sum 1]
 #pragma GCC unroll 4
-        for (int v = 0; v < 4; ++v) {
-            a[v][0] += p0 * ldv(x[v] + i);
-            a[v][1] += p1 * ldv(x[v] + i + 16);
-            a[v][2] += p2 * ldv(x[v] + i + 32);
-            a[v][3] += p3 * ldv(x[v] + i + 48);
+    for (int v = 0; v < NV; ++v) a[v][0] = a[v][1] = a[v][2] = a[v][3] = vf{};
+    for (int i = 0; i < n; i += 32) {
+        const vf p0 = ldv(w0 + i), p1 = ldv(w0 + i + 16), q0 = ldv(w1 + i), q1 = ldv(w1 + i + 16);
+#pragma GCC unroll 4
+        for (int v = 0; v < NV; ++v) {
+            const vf b0 = ldv(x[v] + i), b1 = ldv(x[v] + i + 16);
+            a[v][0] += p0 * b0;
+            a[v][1] += p1 * b1;
+            a[v][2] += q0 * b0;
+            a[v][3] += q1 * b1;
         }
     }
 #pragma GCC unroll 4
-    for (int v = 0; v < 4; ++v) r[v] = hsum((a[v][0] + a[v][1]) + (a[v][2] + a[v][3]));
+    for (int v = 0; v < NV; ++v) {
+        r[2 * v] = hsum(a[v][0] + a[v][1]);
+        r[2 * v + 1] = hsum(a[v][2] + a[v][3]);
+    }
+}
+
+// dots2 over the misses q0 .. q1 of the list order (vector of miss m: base + its
+// row offset), four at a time, then the remainder one at a time; fn(m, r0, r1)
+// takes the two results of each miss in list order.
+template <typename RowOf, typename Fn>
+static inline void dots2_misses(const float *w0, const float *w1, int q0, int q1, const int32_t *order, int n,
+                                RowOf row_of, Fn fn) {
+    int q = q0;
+    for (; q + 4 <= q1; q += 4) {
+        const float *xs[4];
+        for (int v = 0; v < 4; ++v) xs[v] = row_of(order[q + v]);
+        float r[8];
+        dots2<4>(w0, w1, xs, n, r);
+        for (int v = 0; v < 4; ++v) fn(order[q + v], r[2 * v], r[2 * v + 1]);
+    }
+    for (; q < q1; ++q) {
+        const float *xs[1] = {row_of(order[q])};
+        float r[2];
+        dots2<1>(w0, w1, xs, n, r);
+        fn(order[q], r[0], r[1]);
+    }
 }
 
 static inline float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
@@ -223,20 +191,9 @@ void gateup_rows(const HostMissArgs &a, int e, int j0, int j1) {
     for (int j = j0; j < j1; ++j) {
         decode_row(a.bits, cg, sg, d, j, wg);
         decode_row(a.bits, cu, su, d, j, wu);
-        int q = a.gstart[e];
-        for (; q + 2 <= a.gstart[e + 1]; q += 2) {   // two misses per pass over the rows
-            const int m0 = a.order[q], m1 = a.order[q + 1];
-            float r[4];
-            dot2x2(wg, wu, a.u + (int64_t)a.miss_te[2 * m0] * d, a.u + (int64_t)a.miss_te[2 * m1] * d, d, r);
-            a.h[(int64_t)m0 * f + j] = silu_mul(r[0], r[1]);
-            a.h[(int64_t)m1 * f + j] = silu_mul(r[2], r[3]);
-        }
-        for (; q < a.gstart[e + 1]; ++q) {
-            const int m = a.order[q], t = a.miss_te[2 * m];
-            float g, u;
-            dot2(wg, wu, a.u + (int64_t)t * d, d, g, u);
-            a.h[(int64_t)m * f + j] = silu_mul(g, u);
-        }
+        dots2_misses(wg, wu, a.gstart[e], a.gstart[e + 1], a.order, d,
+                     [&](int m) { return a.u + (int64_t)a.miss_te[2 * m] * d; },
+                     [&](int m, float g, float u) { a.h[(int64_t)m * f + j] = silu_mul(g, u); });
     }
 }
 
@@ -247,28 +204,21 @@ void down_cols(const HostMissArgs &a, const int32_t *experts, int ne, int i0, in
     const int64_t mat_bytes = (int64_t)d * f * a.bits / 8, mat_blocks = (int64_t)d * f / 256;
     for (int t = 0; t < a.T; ++t)
         for (int i = i0; i < i1; ++i) a.y_add[(int64_t)t * d + i] = 0.f;
-    alignas(64) float wd[HOST_MAX_F];
+    alignas(64) float wd0[HOST_MAX_F], wd1[HOST_MAX_F];
     for (int x = 0; x < ne; ++x) {
         const int e = experts[x];
         const uint8_t *cd = a.codes + ((int64_t)e * 3 + 2) * mat_bytes;
         const uint16_t *sd = a.scales + (int64_t)e * 3 * mat_blocks + 2 * mat_blocks;
-        for (int i = i0; i < i1; ++i) {
-            decode_row(a.bits, cd, sd, f, i, wd);
-            int q = a.gstart[e];
-            for (; q + 4 <= a.gstart[e + 1]; q += 4) {   // four misses per pass over the row, added in list order
-                const float *hx[4];
-                for (int v = 0; v < 4; ++v) hx[v] = a.h + (int64_t)a.order[q + v] * f;
-                float r[4];
-                dotx4(wd, hx, f, r);
-                for (int v = 0; v < 4; ++v) {
-                    const int m = a.order[q + v];
-                    a.y_add[(int64_t)a.miss_te[2 * m] * d + i] += a.miss_w[m] * r[v];
-                }
-            }
-            for (; q < a.gstart[e + 1]; ++q) {
-                const int m = a.order[q], t = a.miss_te[2 * m];
-                a.y_add[(int64_t)t * d + i] += a.miss_w[m] * dot(wd, a.h + (int64_t)m * f, f);
-            }
+        for (int i = i0; i < i1; i += 2) {   // rows i and i + 1 of Wd (i1 - i0 is even), each column's adds in list order
+            decode_row(a.bits, cd, sd, f, i, wd0);
+            decode_row(a.bits, cd, sd, f, i + 1, wd1);
+            dots2_misses(wd0, wd1, a.gstart[e], a.gstart[e + 1], a.order, f,
+                         [&](int m) { return a.h + (int64_t)m * f; },
+                         [&](int m, float y0, float y1) {
+                             float *yr = a.y_add + (int64_t)a.miss_te[2 * m] * d;
+                             yr[i] += a.miss_w[m] * y0;
+                             yr[i + 1] += a.miss_w[m] * y1;
+                         });
         }
     }
 }
