@@ -64,50 +64,59 @@ static inline uint32_t rd32(const uint8_t *p) {
     return v;
 }
 
-// The 32 codes of one unit, minus c0, as two vectors (places 0-15, 16-31).
+// The 32 codes of one unit as two vectors (places 0-15, 16-31) of integers.
 // 3-bit unit: words A, B, C; places j < 24 are the low 3 bits of nibble
-// j % 8 of word j / 8; places 24 + n gather bit 3 of nibble n of A, B, C.
-static inline void unit_codes3(const uint8_t *p, float c0, vf &lo, vf &hi) {
+// j % 8 of word j / 8; places 24 + n gather bit 3 of nibble n of A, B, C,
+// which one scalar word D holds as its nibble n: then both vectors are two
+// words spread over 8 lanes each, shifted and masked.
+static inline void unit_codes3(const uint8_t *p, vi &lo, vi &hi) {
     const uint32_t A = rd32(p), B = rd32(p + 4), C = rd32(p + 8);
+    const uint32_t D = ((A >> 3) & 0x11111111u) | ((B >> 2) & 0x22222222u) | ((C >> 1) & 0x44444444u);
     const vu sh = {0, 4, 8, 12, 16, 20, 24, 28, 0, 4, 8, 12, 16, 20, 24, 28};
-    const vu sh3 = {0, 4, 8, 12, 16, 20, 24, 28, 3, 7, 11, 15, 19, 23, 27, 31};
     const vu ab = {A, A, A, A, A, A, A, A, B, B, B, B, B, B, B, B};
-    const vu ca = {C, C, C, C, C, C, C, C, A, A, A, A, A, A, A, A};
-    const vu zb = {0, 0, 0, 0, 0, 0, 0, 0, B, B, B, B, B, B, B, B};
-    const vu zc = {0, 0, 0, 0, 0, 0, 0, 0, C, C, C, C, C, C, C, C};
-    const vu m7 = {7, 7, 7, 7, 7, 7, 7, 7, 1, 1, 1, 1, 1, 1, 1, 1};
-    const vu c_lo = (ab >> sh) & 7u;
-    const vu c_hi = ((ca >> sh3) & m7) | (((zb >> sh3) & 1u) << 1) | (((zc >> sh3) & 1u) << 2);
-    lo = __builtin_convertvector((vi)c_lo, vf) - c0;
-    hi = __builtin_convertvector((vi)c_hi, vf) - c0;
+    const vu cd = {C, C, C, C, C, C, C, C, D, D, D, D, D, D, D, D};
+    lo = (vi)((ab >> sh) & 7u);
+    hi = (vi)((cd >> sh) & 7u);
 }
 
 // 2-bit unit: words A (places 0-15) and B (16-31); place j of a word is
 // bits [4 (j % 8) + 2 (j / 8), +2).
-static inline void unit_codes2(const uint8_t *p, float c0, vf &lo, vf &hi) {
+static inline void unit_codes2(const uint8_t *p, vi &lo, vi &hi) {
     const uint32_t A = rd32(p), B = rd32(p + 4);
     const vu sh = {0, 4, 8, 12, 16, 20, 24, 28, 2, 6, 10, 14, 18, 22, 26, 30};
     const vu a = {A, A, A, A, A, A, A, A, A, A, A, A, A, A, A, A};
     const vu b = {B, B, B, B, B, B, B, B, B, B, B, B, B, B, B, B};
-    lo = __builtin_convertvector((vi)((a >> sh) & 3u), vf) - c0;
-    hi = __builtin_convertvector((vi)((b >> sh) & 3u), vf) - c0;
+    lo = (vi)((a >> sh) & 3u);
+    hi = (vi)((b >> sh) & 3u);
 }
 
-// Row r of a packed matrix [out][in] as fp32 weights scale * (code - c0).
+// Row r of a packed matrix [out][in] as fp32 weights scale * (code - c0),
+// formed as code * scale - c0 * scale in one fused multiply-add (both
+// products are exact in fp32, so the result is the exact weight).  Unit
+// (r, c / 32) sits at the row's first unit + (c / 128) * 64 units + (c % 128)
+// / 32 units; the scale of the 256-element block holding (r, c) is read once
+// per block.
 static void decode_row(int bits, const uint8_t *mat, const uint16_t *msc, int in, int r, float *w) {
     const int UB = bits == 3 ? 12 : 8;
     const float c0 = bits == 3 ? 3.5f : 1.5f;
-    const int64_t rowbase = (int64_t)(r >> 4) * (in >> 7);
+    const uint8_t *row = mat + ((int64_t)(r >> 4) * (in >> 7) * 16 + (r & 15)) * 4 * UB;
+    const int64_t e0 = (int64_t)r * in;
+    int64_t blk = -1;
+    vf s = {}, ms = {};
     for (int c = 0; c < in; c += 32) {
-        const int64_t off = ((rowbase + (c >> 7)) * 16 + (r & 15)) * 4 * UB + ((c & 127) >> 5) * UB;
-        vf lo, hi;
-        if (bits == 3) unit_codes3(mat + off, c0, lo, hi);
-        else unit_codes2(mat + off, c0, lo, hi);
-        const float s = half_to_float(msc[((int64_t)r * in + c) >> 8]);
-        lo *= s;
-        hi *= s;
-        memcpy(w + c, &lo, 64);
-        memcpy(w + c + 16, &hi, 64);
+        const uint8_t *u = row + (int64_t)(c >> 7) * 64 * UB + ((c & 127) >> 5) * UB;
+        if (((e0 + c) >> 8) != blk) {
+            blk = (e0 + c) >> 8;
+            const float sv = half_to_float(msc[blk]);
+            s = vf{} + sv;
+            ms = vf{} - c0 * sv;
+        }
+        vi lo, hi;
+        if (bits == 3) unit_codes3(u, lo, hi);
+        else unit_codes2(u, lo, hi);
+        const vf wl = __builtin_convertvector(lo, vf) * s + ms, wh = __builtin_convertvector(hi, vf) * s + ms;
+        memcpy(w + c, &wl, 64);
+        memcpy(w + c + 16, &wh, 64);
     }
 }
 
